@@ -1,0 +1,349 @@
+"""Seeded synthetic decode workloads for paged KV-cache attention.
+
+This module builds inputs only: context lengths, which sequences share a
+prefix, the physical block each logical block lands in, the slot of every
+token to be written, and the q/K/V values.  It holds none of the attention
+arithmetic, and it is the one module that both the GPU path and the CPU
+checker read their inputs from.
+
+Recipe (per workload ``k``, one ``numpy.random.default_rng(seed)``; draws in
+this fixed order):
+
+1. context lengths (the length the measured step's query sees, including the
+   token that step appends);
+2. which sequences share a prefix (where the workload has sharing);
+3. a permutation of the physical block ids, used as the initial free stack
+   (bottom first; blocks are taken from the top, like a LIFO free list);
+4. q for step 0.
+
+K/V values come from counter-keyed streams so they can be drawn in parallel
+and still not depend on the thread count: prefill chunk ``c`` (2048 tokens,
+K then V) uses ``default_rng([seed, 5, c])``; the tokens appended at step
+``s`` use ``default_rng([seed, 6, s, c])``; q for step ``s >= 1`` uses
+``default_rng([seed, 7, s])``.  Values are N(0, 1) drawn in float32; bf16
+workloads round them to bfloat16 (round to nearest, ties to even) and store
+the 16-bit patterns as ``uint16``.
+
+Block assignment: every sequence's prefill (positions ``0 .. ctx-2``) takes
+its blocks in sequence order, then each step's appended token takes a new
+block only when its position starts a block.  A shared prefix is written once,
+by the first member of its group, whose blocks then also head the other
+members' tables.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import math
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+CHUNK_TOKENS = 2048
+
+
+# --------------------------------------------------------------------------
+# The five workloads
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Config:
+    name: str
+    seed: int
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    dtype: str                      # "f32" or "bf16"
+    scale: float
+    description: str
+    partition_size: int = -1        # -1: the library chooses
+    # context lengths: ("fixed", [..]) | ("uniform", lo, hi) | ("const", n)
+    ctx_rule: tuple = ()
+    # prefix sharing: None | ("random_group", n_members, n_shared_blocks, min_ctx)
+    #                       | ("fork", n_prompts, samples_per_prompt, prompt_len)
+    sharing: tuple | None = None
+
+
+CONFIGS = {
+    "tiny_f32": Config(
+        name="tiny_f32", seed=1, num_seqs=4, num_q_heads=4, num_kv_heads=4, head_dim=16,
+        block_size=4, num_blocks=64, max_blocks_per_seq=16, dtype="f32", scale=1 / 4,
+        ctx_rule=("fixed", [5, 17, 33, 64]),
+        description="fp32 tiny decode: 4 sequences (ctx 5/17/33/64), 4 MHA heads, head_dim 16, "
+                    "block 4, 64 physical blocks"),
+    "mha_f32": Config(
+        name="mha_f32", seed=2, num_seqs=32, num_q_heads=8, num_kv_heads=8, head_dim=64,
+        block_size=16, num_blocks=8192, max_blocks_per_seq=129, dtype="f32", scale=1 / 8,
+        ctx_rule=("uniform", 1, 2048), sharing=("random_group", 8, 4, 65),
+        description="fp32 MHA decode: 32 sequences, ctx U[1,2048], 8 heads, head_dim 64, block 16, "
+                    "8192 blocks, 8 sequences share their first 4 blocks"),
+    "gqa_bf16": Config(
+        name="gqa_bf16", seed=3, num_seqs=256, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        block_size=16, num_blocks=65536, max_blocks_per_seq=256, dtype="bf16",
+        scale=1 / math.sqrt(128), ctx_rule=("uniform", 512, 4096),
+        description="bf16 GQA decode (Llama-3-8B layer shape): 256 sequences, ctx U[512,4096], "
+                    "32 q / 8 kv heads, head_dim 128, block 16"),
+    "shared_prefix_bf16": Config(
+        name="shared_prefix_bf16", seed=4, num_seqs=256, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, block_size=16, num_blocks=16384, max_blocks_per_seq=160, dtype="bf16",
+        scale=1 / math.sqrt(128), ctx_rule=("const", 2560), sharing=("fork", 32, 8, 2048),
+        description="bf16 shared-prefix parallel sampling: 32 prompts of 2048 tokens x 8 samples, "
+                    "512 private tokens each (ctx 2560), 32 q / 8 kv heads, head_dim 128, block 16"),
+    "long_split_bf16": Config(
+        name="long_split_bf16", seed=5, num_seqs=16, num_q_heads=64, num_kv_heads=8,
+        head_dim=128, block_size=16, num_blocks=32768, max_blocks_per_seq=2048, dtype="bf16",
+        scale=1 / math.sqrt(128), ctx_rule=("const", 32768), partition_size=512,
+        description="bf16 long-context split decode: 16 sequences x ctx 32768, 64 q / 8 kv heads, "
+                    "head_dim 128, block 16, 512-token partitions"),
+}
+CONFIG_ORDER = ["tiny_f32", "mha_f32", "gqa_bf16", "shared_prefix_bf16", "long_split_bf16"]
+
+
+# --------------------------------------------------------------------------
+# Value helpers
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest, ties to even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal(rng, shape, dtype):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def storage_dtype(dtype: str):
+    return np.uint16 if dtype == "bf16" else np.float32
+
+
+def _workers():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+# --------------------------------------------------------------------------
+# Workload
+# --------------------------------------------------------------------------
+@dataclass
+class Workload:
+    cfg: Config
+    num_steps: int
+    context_lens: np.ndarray            # int32 [B], at step 0 (includes step 0's token)
+    tables: np.ndarray                  # int32 [B, max_blocks], every block the run uses
+    n_blocks_at: list                   # per step: int array [B] of table entries in use
+    prefill_slots: np.ndarray           # int64 [T]
+    prefill_k: np.ndarray               # [T, Hkv, d]
+    prefill_v: np.ndarray
+    step_slots: list                    # per step: int64 [B]
+    step_k: list                        # per step: [B, Hkv, d]
+    step_v: list
+    q: list                             # per step: [B, Hq, d]
+    groups: list = field(default_factory=list)   # shared groups: (members, n_shared_blocks)
+    free_order: np.ndarray | None = None         # initial free stack, bottom first
+
+    def ctx_at(self, step: int) -> np.ndarray:
+        return (self.context_lens + step).astype(np.int32)
+
+    def tables_at(self, step: int) -> np.ndarray:
+        """Block tables as the given step sees them: -1 past the blocks in use."""
+        t = np.full_like(self.tables, -1)
+        n = self.n_blocks_at[step]
+        for b in range(self.cfg.num_seqs):
+            t[b, :n[b]] = self.tables[b, :n[b]]
+        return t
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) + self.num_steps - 1
+
+    def kv_logical_bytes(self, step: int = 0) -> int:
+        c = self.cfg
+        es = 2 if c.dtype == "bf16" else 4
+        return int(self.ctx_at(step).astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * es
+
+    def kv_unique_bytes(self, step: int = 0) -> int:
+        c = self.cfg
+        es = 2 if c.dtype == "bf16" else 4
+        t = self.tables_at(step)
+        ids = np.unique(t[t >= 0])
+        return int(ids.size) * c.block_size * c.num_kv_heads * c.head_dim * 2 * es
+
+
+def _context_lengths(cfg: Config, rng) -> np.ndarray:
+    rule = cfg.ctx_rule
+    if rule[0] == "fixed":
+        return np.asarray(rule[1], dtype=np.int32)
+    if rule[0] == "uniform":
+        return rng.integers(rule[1], rule[2] + 1, size=cfg.num_seqs).astype(np.int32)
+    if rule[0] == "const":
+        return np.full(cfg.num_seqs, rule[1], dtype=np.int32)
+    raise ValueError(rule)
+
+
+
+
+def _draw_tokens(key, n_tokens, hkv, d, dtype, chunk=CHUNK_TOKENS):
+    """K and V for n_tokens tokens; chunk c comes from default_rng(key + [c])
+    (K first, then V), drawn in parallel, independent of the thread count."""
+    sd = storage_dtype(dtype)
+    k = np.empty((n_tokens, hkv, d), dtype=sd)
+    v = np.empty((n_tokens, hkv, d), dtype=sd)
+    n_chunks = (n_tokens + chunk - 1) // chunk
+
+    def one(c):
+        lo, hi = c * chunk, min(n_tokens, (c + 1) * chunk)
+        rng = np.random.default_rng(list(key) + [c])
+        k[lo:hi] = _normal(rng, (hi - lo, hkv, d), dtype)
+        v[lo:hi] = _normal(rng, (hi - lo, hkv, d), dtype)
+
+    if n_chunks <= 1:
+        for c in range(n_chunks):
+            one(c)
+    else:
+        with cf.ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(one, range(n_chunks)))
+    return k, v
+
+
+class _FreeStack:
+    def __init__(self, order):
+        self.stack = [int(x) for x in order]
+
+    def pop(self):
+        if not self.stack:
+            raise RuntimeError("workload needs more physical blocks than the pool holds")
+        return self.stack.pop()
+
+
+def make_workload(name_or_cfg, num_steps: int = 1, share: bool = True,
+                  num_blocks: int | None = None, with_values: bool = True) -> Workload:
+    """Build a workload of ``num_steps`` consecutive decode steps.
+
+    ``share=False`` keeps the same logical content (the same q/K/V values at
+    every position) but gives every sequence private blocks for what would
+    have been shared: the "each sequence its own KV" layout.  It may need a
+    larger ``num_blocks``.  ``with_values=False`` builds the layout only.
+    """
+    cfg = CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
+    if num_blocks is not None:
+        cfg = Config(**{**cfg.__dict__, "num_blocks": int(num_blocks)})
+    B, bs, hkv, d = cfg.num_seqs, cfg.block_size, cfg.num_kv_heads, cfg.head_dim
+    rng = np.random.default_rng(cfg.seed)
+
+    # (1) context lengths
+    ctx = _context_lengths(cfg, rng)
+    if ctx.min() < 1:
+        raise ValueError("every sequence needs at least the token of step 0")
+    # (2) sharing structure: leader[b] holds the values of b's shared prefix
+    leader = np.arange(B)
+    n_shared = np.zeros(B, dtype=np.int64)          # shared prefix, in blocks
+    groups = []
+    if cfg.sharing and cfg.sharing[0] == "random_group":
+        _, n_members, n_sh, min_ctx = cfg.sharing
+        eligible = np.flatnonzero(ctx >= min_ctx)
+        members = np.sort(rng.choice(eligible, size=n_members, replace=False))
+        leader[members] = members[0]
+        n_shared[members] = n_sh
+        groups.append((members.tolist(), int(n_sh)))
+    elif cfg.sharing and cfg.sharing[0] == "fork":
+        _, n_prompts, n_samples, prompt_len = cfg.sharing
+        assert n_prompts * n_samples == B and prompt_len % bs == 0
+        for p in range(n_prompts):
+            members = np.arange(p * n_samples, (p + 1) * n_samples)
+            leader[members] = members[0]
+            n_shared[members] = prompt_len // bs
+            groups.append((members.tolist(), prompt_len // bs))
+    # (3) free stack
+    free_order = rng.permutation(cfg.num_blocks).astype(np.int32)
+    free = _FreeStack(free_order)
+    # (4) q for step 0
+    q0 = _normal(rng, (B, cfg.num_q_heads, d), cfg.dtype)
+
+    max_ctx = int(ctx.max()) + num_steps - 1
+    if (max_ctx + bs - 1) // bs > cfg.max_blocks_per_seq:
+        raise ValueError("max_blocks_per_seq too small for the run")
+    tables = np.full((B, cfg.max_blocks_per_seq), -1, dtype=np.int32)
+    n_tab = np.zeros(B, dtype=np.int64)
+
+    # Prefill, sequence by sequence: positions 0 .. ctx-2.
+    # value_seq/value_pos: the tokens whose K/V values are drawn (a shared
+    # prefix once, under its leader); write_*: the tokens written to the pool.
+    value_seq, value_pos, first_value = [], [], np.zeros(B, dtype=np.int64)
+    write_seq, write_pos, write_src = [], [], []
+    n_values = 0
+    for b in range(B):
+        n_prefill = int(ctx[b]) - 1
+        need = (n_prefill + bs - 1) // bs
+        follower = leader[b] != b
+        first_own = int(n_shared[b]) * bs if follower else 0
+        if follower and share:
+            tables[b, :n_shared[b]] = tables[leader[b], :n_shared[b]]
+            n_tab[b] = n_shared[b]
+        for i in range(int(n_tab[b]), need):
+            tables[b, i] = free.pop()
+        n_tab[b] = max(n_tab[b], need)
+        own = np.arange(first_own, n_prefill, dtype=np.int64)
+        first_value[b] = n_values - first_own
+        value_seq.append(np.full(own.size, b, dtype=np.int64))
+        value_pos.append(own)
+        if follower and not share:
+            pre = np.arange(0, first_own, dtype=np.int64)
+            write_seq.append(np.full(pre.size, b, dtype=np.int64))
+            write_pos.append(pre)
+            write_src.append(first_value[leader[b]] + pre)
+        write_seq.append(np.full(own.size, b, dtype=np.int64))
+        write_pos.append(own)
+        write_src.append(n_values + np.arange(own.size, dtype=np.int64))
+        n_values += own.size
+    write_seq = np.concatenate(write_seq)
+    write_pos = np.concatenate(write_pos)
+    write_src = np.concatenate(write_src)
+
+    # Decode steps: the appended token takes a new block only at a block start.
+    n_blocks_at, step_pos = [], []
+    for s in range(num_steps):
+        pos = ctx.astype(np.int64) - 1 + s
+        for b in range(B):
+            if pos[b] // bs >= n_tab[b]:
+                tables[b, n_tab[b]] = free.pop()
+                n_tab[b] += 1
+        n_blocks_at.append(n_tab.copy())
+        step_pos.append(pos)
+
+    def slots_of(seqs, poss):
+        return tables[seqs, poss // bs].astype(np.int64) * bs + poss % bs
+
+    prefill_slots = slots_of(write_seq, write_pos)
+    step_slots = [slots_of(np.arange(B), p) for p in step_pos]
+
+    sd = storage_dtype(cfg.dtype)
+    if with_values:
+        vk, vv = _draw_tokens([cfg.seed, 5], n_values, hkv, d, cfg.dtype)
+        if np.array_equal(write_src, np.arange(n_values)):
+            pk, pv = vk, vv
+        else:
+            pk, pv = vk[write_src], vv[write_src]
+        sk, sv, qs = [], [], [q0]
+        for s in range(num_steps):
+            k, v = _draw_tokens([cfg.seed, 6, s], B, hkv, d, cfg.dtype)
+            sk.append(k)
+            sv.append(v)
+            if s >= 1:
+                qs.append(_normal(np.random.default_rng([cfg.seed, 7, s]),
+                                  (B, cfg.num_q_heads, d), cfg.dtype))
+    else:
+        pk = pv = np.zeros((0, hkv, d), dtype=sd)
+        sk, sv, qs = [], [], [q0]
+
+    return Workload(cfg=cfg, num_steps=num_steps, context_lens=ctx, tables=tables,
+                    n_blocks_at=n_blocks_at, prefill_slots=prefill_slots, prefill_k=pk,
+                    prefill_v=pv, step_slots=step_slots, step_k=sk, step_v=sv, q=qs,
+                    groups=groups if share else [], free_order=free_order)

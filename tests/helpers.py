@@ -1,0 +1,76 @@
+"""Shared test helpers: building pools and comparing outputs.
+
+Nothing here computes attention; the oracle and the GPU library do that.
+"""
+import numpy as np
+
+from paged_kv_cache_261_amd import synthetic as S
+
+NAN_BITS = {"f32": np.uint32(0x7FC00000), "bf16": np.uint16(0x7FC0)}
+
+
+def empty_pool(cfg, poison=True):
+    """[NB, Hkv, bs, d] K and V pools, every element NaN-poisoned (or zero)."""
+    shape = (cfg.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim)
+    sd = S.storage_dtype(cfg.dtype)
+    k = np.zeros(shape, dtype=sd)
+    v = np.zeros(shape, dtype=sd)
+    if poison:
+        if cfg.dtype == "f32":
+            k.view(np.uint32)[...] = NAN_BITS["f32"]
+            v.view(np.uint32)[...] = NAN_BITS["f32"]
+        else:
+            k[...] = NAN_BITS["bf16"]
+            v[...] = NAN_BITS["bf16"]
+    return k, v
+
+
+def oracle_pool(w, upto_step=0, poison=True):
+    """The oracle's own pool for workload w after the writes of steps 0..upto_step."""
+    from oracle import pao
+    k, v = empty_pool(w.cfg, poison)
+    pao.slot_write(k, v, w.prefill_k, w.prefill_v, w.prefill_slots, w.cfg.block_size)
+    for s in range(upto_step + 1):
+        pao.slot_write(k, v, w.step_k[s], w.step_v[s], w.step_slots[s], w.cfg.block_size)
+    return k, v
+
+
+def to_float(arr, dtype):
+    """Stored values (float32 or bf16 bits) as float64."""
+    if dtype == "bf16":
+        return S.bf16_bits_to_f32(arr).astype(np.float64)
+    return np.asarray(arr, dtype=np.float64)
+
+
+def paginate(k_logical, v_logical, block_size, num_blocks, rng, dtype="f32", poison=True):
+    """Scatter per-sequence contiguous K/V ([n_b, Hkv, d] each) into a paged pool
+    with randomly chosen physical blocks.  Returns (k_cache, v_cache, tables)."""
+    hkv, d = k_logical[0].shape[1], k_logical[0].shape[2]
+    need = [(k.shape[0] + block_size - 1) // block_size for k in k_logical]
+    max_blocks = max(1, max(need))
+    assert sum(need) <= num_blocks
+    ids = rng.permutation(num_blocks)
+    cfg = S.Config(name="adhoc", seed=0, num_seqs=len(k_logical), num_q_heads=hkv,
+                   num_kv_heads=hkv, head_dim=d, block_size=block_size,
+                   num_blocks=num_blocks, max_blocks_per_seq=max_blocks, dtype=dtype,
+                   scale=1.0, description="")
+    kc, vc = empty_pool(cfg, poison)
+    tables = np.full((len(k_logical), max_blocks), -1, dtype=np.int32)
+    nxt = 0
+    for b, (kl, vl) in enumerate(zip(k_logical, v_logical)):
+        for i in range(need[b]):
+            tables[b, i] = ids[nxt]
+            nxt += 1
+        for j in range(kl.shape[0]):
+            kc[tables[b, j // block_size], :, j % block_size, :] = kl[j]
+            vc[tables[b, j // block_size], :, j % block_size, :] = vl[j]
+    return kc, vc, tables
+
+
+def row_rel_err(got, ref):
+    """Per (sequence, head) row: max_i |got - ref| / max_i |ref|."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    return num / np.maximum(den, 1e-300)
