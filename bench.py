@@ -1,0 +1,263 @@
+"""Benchmark: one decode step of PagedAttention on MI355X.
+
+A step is the whole hot path for one batch: the slot write of the step's new
+tokens (pa_reshape_and_cache) followed by PagedAttention decode (pa_decode:
+the per-partition kernel, plus the log-sum-exp reduce in split mode), all on
+one HIP stream, with every input already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+Prints ONE JSON line.  `value` is the achieved KV-read bandwidth of the whole
+step (logical KV bytes the step's queries read / step time, in GB/s);
+`tokens_per_s` is the decode throughput (sequences advanced per second, one
+layer).  `roofline` prices the dominant kernel (the decode kernel) against
+MI355X's 8 TB/s HBM peak with its algorithmic bytes (unique KV blocks + q +
+out + block tables + context lengths) over its average duration, measured
+with HIP events on the launch stream.  `cpu_baseline` times the CPU oracle
+(float64 concatenate-then-attend plus the slot write) on a bounded sample of
+the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved KV-read GB/s (% HBM peak) and tokens/s"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_CONFIG = "gqa_bf16"
+KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_vector.hip", "pa_reduce.hip",
+                  "pa_cache_write.hip", "pa_api.cpp", "pa_internal.h"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--algo", default="auto", choices=["auto", "vector", "mfma"])
+    ap.add_argument("--partition", type=int, default=None,
+                    help="partition size (0 single pass, -1 library choice); default: workload's")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU work for the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_261_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config, algo_name, partition):
+    """HBM traffic per decode launch from committed rocprofv3 counter runs,
+    if they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{config}/{algo_name}/{partition}")
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, target_seconds):
+    """Time the oracle (slot write of the step's tokens + float64
+    concatenate-then-attend) on a bounded prefix of the batch, all cores."""
+    from oracle import pao
+    c = w.cfg
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    kh = np.zeros((c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim),
+                  dtype=w.prefill_k.dtype)
+    vh = np.zeros_like(kh)
+    pao.slot_write(kh, vh, w.prefill_k, w.prefill_v, w.prefill_slots, c.block_size)
+    ctx, tab, q = w.ctx_at(0), w.tables_at(0), w.q[0]
+    es = 2 if c.dtype == "bf16" else 4
+
+    def run(n):
+        t = time.perf_counter()
+        pao.slot_write(kh, vh, w.step_k[0][:n], w.step_v[0][:n], w.step_slots[0][:n],
+                       c.block_size)
+        pao.decode_concat(q[:n], kh, vh, tab[:n], ctx[:n], c.scale, nthreads=cores)
+        return time.perf_counter() - t
+
+    n = min(c.num_seqs, max(1, cores))
+    dt = run(n)
+    while n < c.num_seqs and dt < target_seconds / 4:
+        n = min(c.num_seqs, n * 2)
+        dt = run(n)
+    if n < c.num_seqs and dt < target_seconds:
+        n = min(c.num_seqs, max(n, int(n * target_seconds / max(dt, 1e-3))))
+        dt = run(n)
+    kv = int(ctx[:n].astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * es
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {c.num_seqs} sequences of {c.name} "
+                      f"(sum ctx {int(ctx[:n].sum())}), one step, {dt:.2f} s",
+            "tokens_per_s": round(n / dt, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"metric": METRIC, "error": "this build measures one GPU only: the "
+                          "decode path has no multi-GPU mode; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_261_amd import pa
+    from paged_kv_cache_261_amd import synthetic as S
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    algo = {"auto": pa.PA_ALGO_AUTO, "vector": pa.PA_ALGO_VECTOR, "mfma": pa.PA_ALGO_MFMA}[args.algo]
+
+    log(f"building workload {args.config}")
+    w = S.make_workload(args.config)
+    c = w.cfg
+    tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+    k_cache = torch.zeros(shape, dtype=tdt, device=dev)
+    v_cache = torch.zeros(shape, dtype=tdt, device=dev)
+    pa.pa_reshape_and_cache(dev_t(w.prefill_k), dev_t(w.prefill_v), k_cache, v_cache,
+                            dev_t(w.prefill_slots))
+    q = dev_t(w.q[0])
+    new_k, new_v = dev_t(w.step_k[0]), dev_t(w.step_v[0])
+    slots = dev_t(w.step_slots[0])
+    ctx_h = w.ctx_at(0)
+    tables = dev_t(w.tables_at(0))
+    ctx = dev_t(ctx_h)
+    max_ctx = int(ctx_h.max())
+    out = torch.empty_like(q)
+    part_req = c.partition_size if args.partition is None else args.partition
+    part = (pa.pa_decode_auto_partition(c.num_seqs, c.num_kv_heads, c.head_dim, c.block_size,
+                                        max_ctx, pa.dtype_code(q))
+            if part_req == -1 else part_req)
+    ws = pa.workspace_for(q, k_cache, max_ctx, part)
+    torch.cuda.synchronize()
+    log(f"workload ready: batch {c.num_seqs}, sum ctx {int(ctx_h.sum())}, partition {part}, "
+        f"algo {args.algo}")
+
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        pa.pa_reshape_and_cache(new_k, new_v, k_cache, v_cache, slots, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        if part == 0:
+            pa.pa_decode(out, q, k_cache, v_cache, tables, ctx, c.scale, max_ctx, 0, None, algo,
+                         stream=stream)
+            if evs is not None:
+                evs[2].record(stream)
+                evs[3].record(stream)
+        else:
+            pa.pa_decode_partitions(out, q, k_cache, v_cache, tables, ctx, c.scale, max_ctx, part,
+                                    ws, algo, stream=stream)
+            if evs is not None:
+                evs[2].record(stream)
+            pa.pa_decode_reduce(out, ctx, max_ctx, part, ws, stream=stream)
+            if evs is not None:
+                evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # (1) wall clock over exactly K steps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps: {wall * 1e3:.2f} ms")
+
+    # (2) per-kernel durations with HIP events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    t_write = [e[0].elapsed_time(e[1]) for e in evs]
+    t_main = [e[1].elapsed_time(e[2]) for e in evs]
+    t_reduce = [e[2].elapsed_time(e[3]) for e in evs]
+    t_step = [e[0].elapsed_time(e[3]) for e in evs]
+
+    es = 2 if c.dtype == "bf16" else 4
+    kv_logical = w.kv_logical_bytes(0)
+    kv_unique = w.kv_unique_bytes(0)
+    qo_bytes = 2 * c.num_seqs * c.num_q_heads * c.head_dim * es
+    table_bytes = int(((ctx_h + c.block_size - 1) // c.block_size).sum()) * 4 + 4 * c.num_seqs
+    decode_alg = kv_unique + qo_bytes + table_bytes
+    ms_step = wall / args.steps * 1e3
+    main_ms = statistics.mean(t_main)
+    achieved = decode_alg / (main_ms * 1e-3) / 1e9
+    algo_name = args.algo
+    traffic = load_traffic(args.config, algo_name, part)
+
+    result = {
+        "metric": METRIC,
+        "value": round(kv_logical / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {"workload": c.name, "description": c.description, "batch": c.num_seqs,
+                   "num_q_heads": c.num_q_heads, "num_kv_heads": c.num_kv_heads,
+                   "head_dim": c.head_dim, "block_size": c.block_size,
+                   "sum_context": int(ctx_h.sum()), "max_context": max_ctx,
+                   "partition_size": part, "algo": algo_name, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(c.num_seqs / (ms_step * 1e-3), 1),
+        "hbm_peak_frac_step": round(kv_logical / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels_ms": {"reshape_and_cache": round(statistics.mean(t_write), 5),
+                       "decode": round(main_ms, 5),
+                       "reduce": round(statistics.mean(t_reduce), 5),
+                       "step_events": round(statistics.mean(t_step), 5),
+                       "decode_p10": round(float(np.percentile(t_main, 10)), 5),
+                       "decode_p90": round(float(np.percentile(t_main, 90)), 5)},
+        "bytes": {"kv_logical": kv_logical, "kv_unique": kv_unique,
+                  "decode_algorithmic": decode_alg},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode (per-partition kernel)"},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+/*
+ * pa.h -- paged KV-cache decode for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  It does two things:
+ *
+ *   1. the slot write: append new tokens' K/V into their physical slots of a
+ *      block-paged cache (pa_reshape_and_cache);
+ *   2. PagedAttention decode: each query head attends over its sequence's
+ *      cached K/V, which is scattered over fixed-size physical blocks and
+ *      reached through a per-sequence block table (pa_decode, and its two
+ *      split-context phases pa_decode_partitions / pa_decode_reduce).
+ *
+ * Sources (cited by page title and the named part of the page):
+ *   "PagedAttention实现" (ainanfeng.cn project page): KVBlock (a block holds
+ *       block_size token slots of K and of V), PageTable (logical block ->
+ *       physical block), PagedKVManager::write_kv (a token at position pos is
+ *       in logical block pos / block_size at offset pos % block_size).
+ *   "CS349E 第 7 讲 01_paged_attention.py" (lecture 7 script): demo 2, paper
+ *       eq. 4 -- scores block by block, one softmax over the whole context,
+ *       V multiplied in block by block; paged and contiguous KV give the same
+ *       result.
+ *   "04 - Paged Attention 实现进度": section A.2 (block_tables is
+ *       [batch, max_blocks_per_seq], slot_mapping is [total_tokens]),
+ *       section B.2 (Context: slot_mapping maps token -> physical slot, i.e.
+ *       block id and offset; context_lens is each sequence's current length;
+ *       block_tables records each sequence's blocks in order), section B.3
+ *       (block size 16).
+ *
+ * Conventions (all entry points):
+ *   - Every pointer argument named as a tensor is a DEVICE pointer to a
+ *     contiguous, row-major buffer that the caller allocated and owns.  The
+ *     library keeps no reference after the call returns.
+ *   - pa_reshape_and_cache, pa_decode, pa_decode_partitions and
+ *     pa_decode_reduce never allocate device memory and never synchronise:
+ *     they validate their arguments on the host, enqueue kernels on `stream`
+ *     (a hipStream_t; NULL = the default stream) and return.  Results are
+ *     ready when the stream reaches that point.
+ *   - Return value: PA_OK (0) or a negative PA_ERR_* status; nothing is
+ *     enqueued when a status other than PA_OK is returned for an argument
+ *     error.  The library never prints and never aborts.
+ *   - Every tensor pointer (and the workspace) must be 16-byte aligned.
+ *   - dtype: PA_F32 (float) or PA_BF16 (bfloat16 bit patterns).  q, out,
+ *     new K/V and both caches share one dtype.  Arithmetic is float32.
+ *   - Cache layout, for K and for V separately:
+ *         cache[num_blocks][num_kv_heads][block_size][head_dim]
+ *     so one (block, KV head) tile is block_size*head_dim contiguous
+ *     elements.
+ *   - Device-side integer data (slots, block ids, context lengths) is
+ *     trusted for correctness but bounded for safety: a slot outside
+ *     [0, num_blocks*block_size) is not written, a block-table entry outside
+ *     [0, num_blocks) is not read (the tokens it would hold are left out),
+ *     and a context length is clamped to [0, max_context_len].  Such inputs
+ *     give unspecified results but no access outside the caller's buffers.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+enum {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,         /* a required pointer is NULL                      */
+    PA_ERR_SHAPE = -2,        /* sizes inconsistent or out of range              */
+    PA_ERR_UNSUPPORTED = -3,  /* head_dim / block_size / dtype / group size      */
+    PA_ERR_WORKSPACE = -4,    /* workspace missing or smaller than required      */
+    PA_ERR_LAUNCH = -5,       /* the HIP runtime refused a kernel launch         */
+    PA_ERR_ALGO = -6,         /* requested kernel variant cannot run this shape  */
+    PA_ERR_ALIGN = -7         /* a tensor pointer is not 16-byte aligned          */
+};
+
+/* Kernel variants for pa_decode / pa_decode_partitions. */
+enum {
+    PA_ALGO_AUTO = 0,   /* matrix-core kernel where it applies, else vector    */
+    PA_ALGO_VECTOR = 1, /* vector-ALU kernel (any supported shape)             */
+    PA_ALGO_MFMA = 2    /* matrix-core kernel: bf16, head_dim 128,
+                           block_size >= 16, group size <= 16                  */
+};
+
+/*
+ * Slot write ("PagedAttention实现", write_kv; "04 - Paged Attention 实现进度",
+ * section A.2 slot_mapping).  For every token t with s = slot_mapping[t] >= 0:
+ *     block = s / block_size,  offset = s % block_size,
+ *     k_cache[block][g][offset][:] = k[t][g][:]   for every KV head g,
+ * and the same for V.  The copy is bit-exact (no conversion).  Negative
+ * slots mark padding tokens and are skipped.
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim]             (in)
+ *   k_cache,
+ *   v_cache       [num_blocks][num_kv_heads][block_size][head_dim] (in/out)
+ *   slot_mapping  [num_tokens] int64                               (in)
+ *
+ * Slots within one call must be distinct (two tokens writing one slot race).
+ * Supported: head_dim in {16, 32, 64, 128, 256}; block_size a power of two
+ * in [1, 256]; dtype PA_F32 or PA_BF16.  num_tokens == 0 is a no-op.
+ */
+int pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_cache,
+                         const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
+                         int head_dim, int num_blocks, int block_size, int dtype,
+                         void *stream);
+
+/*
+ * Partition size the library uses when pa_decode / pa_decode_partitions get
+ * partition_size == -1 for these sizes: 0 (single pass, no workspace) or a
+ * multiple of block_size.  A pure function of its arguments.
+ */
+int pa_decode_auto_partition(int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                             int max_context_len, int dtype);
+
+/*
+ * Bytes of device workspace pa_decode needs (0 in single-pass mode).
+ * partition_size as for pa_decode (-1 resolves through
+ * pa_decode_auto_partition with these same arguments).  Returns 0 for
+ * invalid sizes as well.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                int block_size, int max_context_len, int partition_size,
+                                int dtype);
+
+/*
+ * PagedAttention decode ("CS349E 第 7 讲 01_paged_attention.py", demo 2,
+ * paper eq. 4).  One query token per sequence b, query head h, KV head
+ * g = h / (num_q_heads / num_kv_heads), n = context_lens[b]:
+ *     s_j = scale * dot(q[b][h], K_b[j]),   j < n
+ *     out[b][h] = sum_j softmax(s)_j * V_b[j]
+ * where K_b[j] is element g of the token at logical position j, found at
+ * block block_tables[b][j / block_size], offset j % block_size.  One
+ * softmax is taken over the whole context.  n == 0 gives zeros.
+ *
+ *   out           [num_seqs][num_q_heads][head_dim]                 (out)
+ *   q             [num_seqs][num_q_heads][head_dim]                 (in)
+ *   k_cache,
+ *   v_cache       [num_blocks][num_kv_heads][block_size][head_dim]  (in)
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32              (in)
+ *   context_lens  [num_seqs] int32, tokens visible to this step's query,
+ *                 including the one appended by this step's slot write (in)
+ *   max_context_len  an upper bound on context_lens (sizes the workspace)
+ *   scale         softmax scale (usually 1/sqrt(head_dim))
+ *   partition_size   0: single pass, one work unit per (sequence, KV head);
+ *                 -1: the library chooses (pa_decode_auto_partition);
+ *                 otherwise a multiple of block_size: the context is split
+ *                 into partitions of that many tokens, each reduced
+ *                 separately, then merged by log-sum-exp (split-context
+ *                 decode: pa_decode_partitions followed by pa_decode_reduce).
+ *   workspace     device scratch of at least pa_decode_workspace_size(...)
+ *                 bytes in split mode (ignored in single-pass mode).  Calls
+ *                 that share a workspace must be ordered on one stream.
+ *   algo          PA_ALGO_AUTO, PA_ALGO_VECTOR or PA_ALGO_MFMA.
+ *
+ * Supported: head_dim in {16, 32, 64, 128, 256}; block_size a power of two in
+ * [1, 256]; num_q_heads a multiple of num_kv_heads with a group size of at
+ * most 16; dtype PA_F32 or PA_BF16.  Write this step's token with
+ * pa_reshape_and_cache earlier on the same stream.
+ */
+int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+              int num_q_heads, int num_kv_heads, int head_dim, int num_blocks, int block_size,
+              int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
+              void *workspace, size_t workspace_bytes, int dtype, int algo, void *stream);
+
+/*
+ * Phase 1 of split-context decode: per (sequence, query head, partition p)
+ * of partition_size tokens (a positive multiple of block_size), the running
+ * max m_p (base-2 log domain: scores times scale*log2(e)), the sum
+ * l_p = sum_j 2^(s_j - m_p) and the unnormalised acc_p = sum_j 2^(s_j - m_p)
+ * V[j] go to the workspace.  A sequence with a single partition has its
+ * final output written to `out` directly.  Same arguments as pa_decode.
+ *
+ * Workspace layout (float32), NP = ceil(max_context_len / partition_size):
+ *     m   [num_seqs][num_q_heads][NP]
+ *     l   [num_seqs][num_q_heads][NP]
+ *     acc [num_seqs][num_q_heads][NP][head_dim]
+ * each array starting at a 256-byte aligned offset, in that order.  This is
+ * the exchange format for splitting one sequence's context across devices.
+ */
+int pa_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
+                         const int32_t *block_tables, const int32_t *context_lens,
+                         int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                         int num_blocks, int block_size, int max_blocks_per_seq,
+                         int max_context_len, float scale, int partition_size,
+                         void *workspace, size_t workspace_bytes, int dtype, int algo,
+                         void *stream);
+
+/*
+ * Phase 2 of split-context decode: for every sequence with more than one
+ * partition, merge the partitions in ascending order:
+ *     M = max_p m_p,  w_p = 2^(m_p - M),
+ *     out = (sum_p w_p acc_p) / (sum_p w_p l_p).
+ * Sequences with one partition are left alone (phase 1 wrote them).
+ */
+int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int num_q_heads,
+                     int head_dim, int max_context_len, int partition_size,
+                     const void *workspace, size_t workspace_bytes, int dtype, void *stream);
+
+/* A static, human-readable name for a status code. */
+const char *pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

@@ -1,0 +1,268 @@
+// pa_api.cpp -- the C ABI of include/pa.h: host-side validation, choice of
+// kernel and partitioning, and kernel launches on the caller's stream.
+// Nothing here allocates device memory or synchronises.
+#include "pa.h"
+
+#include <math.h>
+
+#include "pa_internal.h"
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+    int r = 0;
+    while ((1 << r) < x) r++;
+    return r;
+}
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+bool block_size_ok(int bs) { return is_pow2(bs) && bs <= 256; }
+
+bool dtype_ok(int dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Resolve the partition size: 0 = single pass, else a multiple of block_size.
+int resolve_partition(int partition_size, int num_seqs, int num_kv_heads, int head_dim,
+                      int block_size, int max_context_len, int dtype) {
+    if (partition_size == -1)
+        return pa_decode_auto_partition(num_seqs, num_kv_heads, head_dim, block_size,
+                                        max_context_len, dtype);
+    return partition_size;
+}
+
+struct WorkspaceLayout {
+    size_t m_off, l_off, acc_off, total;
+    int num_partitions;
+};
+
+WorkspaceLayout layout(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
+                       int partition) {
+    WorkspaceLayout w{};
+    w.num_partitions = max_context_len <= 0 ? 1 : (max_context_len + partition - 1) / partition;
+    const size_t rows = (size_t)num_seqs * num_q_heads * w.num_partitions;
+    w.m_off = 0;
+    w.l_off = round256(rows * sizeof(float));
+    w.acc_off = w.l_off + round256(rows * sizeof(float));
+    w.total = w.acc_off + round256(rows * head_dim * sizeof(float));
+    return w;
+}
+
+struct DecodeArgs {
+    void *out;
+    const void *q, *k_cache, *v_cache;
+    const int32_t *block_tables, *context_lens;
+    int num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size;
+    int max_blocks_per_seq, max_context_len;
+    float scale;
+    int dtype, algo;
+};
+
+int validate_decode(const DecodeArgs &a) {
+    if (a.num_seqs < 0 || a.num_q_heads <= 0 || a.num_kv_heads <= 0 || a.num_blocks <= 0 ||
+        a.max_blocks_per_seq <= 0 || a.max_context_len < 0)
+        return PA_ERR_SHAPE;
+    if (!dtype_ok(a.dtype) || !head_dim_ok(a.head_dim) || !block_size_ok(a.block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (a.num_q_heads % a.num_kv_heads != 0) return PA_ERR_SHAPE;
+    if (a.num_q_heads / a.num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)a.max_context_len > (int64_t)a.max_blocks_per_seq * a.block_size)
+        return PA_ERR_SHAPE;
+    if (a.algo != PA_ALGO_AUTO && a.algo != PA_ALGO_VECTOR && a.algo != PA_ALGO_MFMA)
+        return PA_ERR_ALGO;
+    if (a.num_seqs == 0) return PA_OK;
+    if (!a.out || !a.q || !a.k_cache || !a.v_cache || !a.block_tables || !a.context_lens)
+        return PA_ERR_NULL;
+    if (!aligned16(a.out) || !aligned16(a.q) || !aligned16(a.k_cache) || !aligned16(a.v_cache))
+        return PA_ERR_ALIGN;
+    return PA_OK;
+}
+
+bool mfma_applies(const DecodeArgs &a) {
+    return a.dtype == PA_BF16 && a.head_dim == 128 && a.block_size >= 16 &&
+           a.num_q_heads / a.num_kv_heads <= 16;
+}
+
+// Phase 1 (or the whole decode when num_partitions == 1).
+int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *ws_m,
+                 float *ws_l, float *ws_acc, hipStream_t stream) {
+    const int64_t units = (int64_t)num_partitions * a.num_kv_heads * a.num_seqs;
+    if (units > 0x7fffffff) return PA_ERR_SHAPE;
+    bool use_mfma;
+    if (a.algo == PA_ALGO_MFMA) {
+        if (!mfma_applies(a)) return PA_ERR_ALGO;
+        use_mfma = true;
+    } else {
+        use_mfma = a.algo == PA_ALGO_AUTO && mfma_applies(a);
+    }
+    pa::DecodeParams p{};
+    p.out = a.out;
+    p.q = a.q;
+    p.k_cache = a.k_cache;
+    p.v_cache = a.v_cache;
+    p.block_tables = a.block_tables;
+    p.context_lens = a.context_lens;
+    p.ws_m = ws_m;
+    p.ws_l = ws_l;
+    p.ws_acc = ws_acc;
+    p.num_seqs = a.num_seqs;
+    p.num_q_heads = a.num_q_heads;
+    p.num_kv_heads = a.num_kv_heads;
+    p.group = a.num_q_heads / a.num_kv_heads;
+    p.num_blocks = a.num_blocks;
+    p.log2_block = ilog2(a.block_size);
+    p.max_blocks_per_seq = a.max_blocks_per_seq;
+    p.max_context_len = a.max_context_len;
+    p.partition_size = partition;
+    p.num_partitions = num_partitions;
+    p.scale_log2 = a.scale * 1.4426950408889634f;
+    p.num_units = (int)units;
+    const hipError_t e = use_mfma ? pa::launch_decode_mfma(p, stream)
+                                  : pa::launch_decode_vector(p, a.head_dim, a.dtype, stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(int status) {
+    switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "sizes inconsistent or out of range";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype or group size";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_ALGO: return "requested kernel variant does not support this shape";
+    case PA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    default: return "unknown status";
+    }
+}
+
+int pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_cache,
+                         const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
+                         int head_dim, int num_blocks, int block_size, int dtype, void *stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || !block_size_ok(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_ALIGN;
+    const hipError_t e = pa::launch_cache_write(k, v, k_cache, v_cache, slot_mapping, num_tokens,
+                                                num_kv_heads, head_dim, num_blocks,
+                                                ilog2(block_size), dtype == PA_BF16 ? 2 : 4,
+                                                (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_decode_auto_partition(int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                             int max_context_len, int dtype) {
+    (void)num_seqs;
+    (void)num_kv_heads;
+    (void)head_dim;
+    (void)dtype;
+    if (!block_size_ok(block_size)) return 0;
+    const int partition = block_size > 512 ? block_size : 512;
+    return max_context_len > partition ? partition : 0;
+}
+
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                int block_size, int max_context_len, int partition_size,
+                                int dtype) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len < 0 || !block_size_ok(block_size))
+        return 0;
+    const int partition = resolve_partition(partition_size, num_seqs, num_kv_heads, head_dim,
+                                            block_size, max_context_len, dtype);
+    if (partition <= 0 || partition % block_size) return 0;
+    return layout(num_seqs, num_q_heads, head_dim, max_context_len, partition).total;
+}
+
+int pa_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
+                         const int32_t *block_tables, const int32_t *context_lens,
+                         int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                         int num_blocks, int block_size, int max_blocks_per_seq,
+                         int max_context_len, float scale, int partition_size,
+                         void *workspace, size_t workspace_bytes, int dtype, int algo,
+                         void *stream) {
+    const DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                       max_blocks_per_seq, max_context_len, scale, dtype, algo};
+    int rc = validate_decode(a);
+    if (rc != PA_OK) return rc;
+    const int partition = resolve_partition(partition_size, num_seqs, num_kv_heads, head_dim,
+                                            block_size, max_context_len, dtype);
+    if (partition <= 0 || partition % block_size) return PA_ERR_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, max_context_len, partition);
+    if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_ALIGN;
+    char *ws = (char *)workspace;
+    return launch_units(a, partition, w.num_partitions, (float *)(ws + w.m_off),
+                        (float *)(ws + w.l_off), (float *)(ws + w.acc_off), (hipStream_t)stream);
+}
+
+int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int num_q_heads,
+                     int head_dim, int max_context_len, int partition_size,
+                     const void *workspace, size_t workspace_bytes, int dtype, void *stream) {
+    if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_size <= 0)
+        return PA_ERR_SHAPE;
+    if (!dtype_ok(dtype) || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !context_lens) return PA_ERR_NULL;
+    const WorkspaceLayout w =
+        layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size);
+    if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace) || !aligned16(out)) return PA_ERR_ALIGN;
+    const char *ws = (const char *)workspace;
+    pa::ReduceParams p{};
+    p.out = out;
+    p.context_lens = context_lens;
+    p.ws_m = (const float *)(ws + w.m_off);
+    p.ws_l = (const float *)(ws + w.l_off);
+    p.ws_acc = (const float *)(ws + w.acc_off);
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.head_dim = head_dim;
+    p.max_context_len = max_context_len;
+    p.partition_size = partition_size;
+    p.num_partitions = w.num_partitions;
+    return pa::launch_reduce(p, dtype, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+              int num_q_heads, int num_kv_heads, int head_dim, int num_blocks, int block_size,
+              int max_blocks_per_seq, int max_context_len, float scale, int partition_size,
+              void *workspace, size_t workspace_bytes, int dtype, int algo, void *stream) {
+    const DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                       max_blocks_per_seq, max_context_len, scale, dtype, algo};
+    int rc = validate_decode(a);
+    if (rc != PA_OK) return rc;
+    const int partition = resolve_partition(partition_size, num_seqs, num_kv_heads, head_dim,
+                                            block_size, max_context_len, dtype);
+    if (partition < 0 || (partition > 0 && partition % block_size)) return PA_ERR_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (partition == 0) {
+        // single pass: one unit per (sequence, KV head) covering the whole context
+        const int whole = max_context_len > 0 ? max_context_len : 1;
+        return launch_units(a, whole, 1, nullptr, nullptr, nullptr, (hipStream_t)stream);
+    }
+    rc = pa_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                              max_blocks_per_seq, max_context_len, scale, partition, workspace,
+                              workspace_bytes, dtype, algo, stream);
+    if (rc != PA_OK) return rc;
+    return pa_decode_reduce(out, context_lens, num_seqs, num_q_heads, head_dim, max_context_len,
+                            partition, workspace, workspace_bytes, dtype, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// pa_internal.h -- shared declarations of the paged-decode library's
+// kernels and launchers (not installed; the public ABI is include/pa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;   // CDNA wavefront width
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
+
+// Everything a decode kernel needs, passed by value as one kernel argument.
+struct DecodeParams {
+    void *out;
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    float *ws_m;              // [B][Hq][NP]       (split mode only)
+    float *ws_l;              // [B][Hq][NP]
+    float *ws_acc;            // [B][Hq][NP][D]
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int group;                // num_q_heads / num_kv_heads
+    int num_blocks;
+    int log2_block;           // block_size = 1 << log2_block
+    int max_blocks_per_seq;
+    int max_context_len;
+    int partition_size;       // tokens per work unit (single pass: >= max_context_len)
+    int num_partitions;       // NP
+    float scale_log2;         // scale * log2(e): scores are kept in base-2 log domain
+    int num_units;            // num_partitions * num_kv_heads * num_seqs
+};
+
+struct ReduceParams {
+    void *out;
+    const int32_t *context_lens;
+    const float *ws_m;
+    const float *ws_l;
+    const float *ws_acc;
+    int num_seqs;
+    int num_q_heads;
+    int head_dim;
+    int max_context_len;
+    int partition_size;
+    int num_partitions;
+};
+
+// Work-unit numbering shared by the decode kernels.  Workgroups are handed
+// to the 8 XCDs round-robin (workgroup w runs on XCD w % 8); this remaps the
+// workgroup id so that consecutive logical units run on the same XCD at about
+// the same time.  Units are numbered with the sequence fastest, so the
+// samples of one prompt (adjacent sequences sharing prefix blocks) reading
+// the same (KV head, partition) meet in one XCD's L2.
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+    const int q = n / kNumXcd, r = n % kNumXcd;
+    const int x = w % kNumXcd, slot = w / kNumXcd;
+    return x * q + (x < r ? x : r) + slot;
+}
+
+struct Unit {
+    int b, g, part;
+};
+
+__device__ __forceinline__ Unit unit_of(int u, int num_seqs, int num_kv_heads) {
+    Unit t;
+    t.b = u % num_seqs;
+    const int rest = u / num_seqs;
+    t.g = rest % num_kv_heads;
+    t.part = rest / num_kv_heads;
+    return t;
+}
+
+__device__ __forceinline__ int clamp_ctx(int n, int max_context_len) {
+    return n < 0 ? 0 : (n > max_context_len ? max_context_len : n);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Launchers: validate nothing (pa_api.cpp does), enqueue, return hipError_t.
+hipError_t launch_cache_write(const void *k, const void *v, void *k_cache, void *v_cache,
+                              const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
+                              int head_dim, int num_blocks, int log2_block, int elem_bytes,
+                              hipStream_t stream);
+
+hipError_t launch_decode_vector(const DecodeParams &p, int head_dim, int dtype,
+                                hipStream_t stream);
+
+hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
+
+hipError_t launch_reduce(const ReduceParams &p, int dtype, hipStream_t stream);
+
+}  // namespace pa

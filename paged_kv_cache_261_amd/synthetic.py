@@ -12,9 +12,12 @@ this fixed order):
 1. context lengths (the length the measured step's query sees, including the
    token that step appends);
 2. which sequences share a prefix (where the workload has sharing);
-3. a permutation of the physical block ids, used as the initial free stack
-   (bottom first; blocks are taken from the top, like a LIFO free list);
-4. q for step 0.
+3. q for step 0.
+
+The initial free stack (bottom first; blocks are taken from the top, like a
+LIFO free list) is a permutation of the physical block ids drawn from its own
+stream, ``default_rng([seed, 3])``, so a variant with a different pool size
+keeps every other draw.
 
 K/V values come from counter-keyed streams so they can be drawn in parallel
 and still not depend on the thread count: prefill chunk ``c`` (2048 tokens,
@@ -261,11 +264,11 @@ def make_workload(name_or_cfg, num_steps: int = 1, share: bool = True,
             leader[members] = members[0]
             n_shared[members] = prompt_len // bs
             groups.append((members.tolist(), prompt_len // bs))
-    # (3) free stack
-    free_order = rng.permutation(cfg.num_blocks).astype(np.int32)
-    free = _FreeStack(free_order)
-    # (4) q for step 0
+    # (3) q for step 0
     q0 = _normal(rng, (B, cfg.num_q_heads, d), cfg.dtype)
+    # free stack, from its own stream
+    free_order = np.random.default_rng([cfg.seed, 3]).permutation(cfg.num_blocks).astype(np.int32)
+    free = _FreeStack(free_order)
 
     max_ctx = int(ctx.max()) + num_steps - 1
     if (max_ctx + bs - 1) // bs > cfg.max_blocks_per_seq:

@@ -1,0 +1,133 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/pa.h declares, and rejects bad arguments on the host before any
+launch.  No kernel runs here."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+LIB = os.path.join(ROOT, "paged_kv_cache_261_amd", "libpa.so")
+
+OK, NULL, SHAPE, UNSUP, WS, LAUNCH, ALGO, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char \*)\s*(pa_\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from paged_kv_cache_261_amd import build
+        build.build()
+    from paged_kv_cache_261_amd import pa
+    return pa.lib
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"pa_reshape_and_cache", "pa_decode", "pa_decode_partitions",
+                          "pa_decode_reduce", "pa_decode_workspace_size",
+                          "pa_decode_auto_partition", "pa_status_string"}
+    raw = C.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(lib):
+    from paged_kv_cache_261_amd import pa
+    for code in (OK, NULL, SHAPE, UNSUP, WS, LAUNCH, ALGO, ALIGN):
+        assert pa.status_string(code) not in ("", "unknown status")
+    assert pa.status_string(12345) == "unknown status"
+
+
+def test_workspace_size_and_auto_partition(lib):
+    from paged_kv_cache_261_amd import pa
+    # single pass needs no workspace
+    assert pa.pa_decode_workspace_size(4, 4, 4, 16, 4, 64, 0, 0) == 0
+    # long-context split: 16 seqs x 64 heads x 64 partitions x (128 + 2) floats
+    n = pa.pa_decode_workspace_size(16, 64, 8, 128, 16, 32768, 512, 1)
+    rows = 16 * 64 * 64
+    assert n >= rows * (128 + 2) * 4 and n < rows * (128 + 2) * 4 + 3 * 256
+    # auto: a partition size that is a multiple of the block size, or single pass
+    for bs in (1, 4, 16, 64, 256):
+        for ctx in (1, 100, 512, 513, 4096, 32768):
+            p = pa.pa_decode_auto_partition(16, 8, 128, bs, ctx, 1)
+            assert p == 0 or (p % bs == 0 and p > 0)
+            ws = pa.pa_decode_workspace_size(16, 64, 8, 128, bs, ctx, -1, 1)
+            assert (ws == 0) == (p == 0)
+    assert pa.pa_decode_workspace_size(1, 1, 1, 128, 16, 100, 24, 1) == 0   # not a multiple
+
+
+# Every call below must be refused by host validation; the fake addresses are
+# never dereferenced.  Skipped where a GPU is present, so that a validation
+# bug can never turn into a kernel launch on fake addresses.
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+needs_no_gpu = pytest.mark.skipif(not _no_gpu(),
+                                  reason="fake-pointer validation tests run only without a GPU")
+A = C.c_void_p(0x10000)       # 16-byte aligned fake address
+MIS = C.c_void_p(0x10004)     # misaligned fake address
+Z = C.c_void_p(0)
+
+
+def decode_call(lib, fn="pa_decode", **kw):
+    a = dict(out=A, q=A, kc=A, vc=A, bt=A, cl=A, B=2, Hq=8, Hkv=2, d=128, NB=64, bs=16, MB=8,
+             max_ctx=100, scale=0.1, part=0, ws=Z, wsb=0, dtype=1, algo=0, stream=Z)
+    a.update(kw)
+    return getattr(lib, fn)(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["B"],
+                            a["Hq"], a["Hkv"], a["d"], a["NB"], a["bs"], a["MB"], a["max_ctx"],
+                            a["scale"], a["part"], a["ws"], a["wsb"], a["dtype"], a["algo"],
+                            a["stream"])
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=48), UNSUP), (dict(d=0), UNSUP), (dict(bs=12), UNSUP), (dict(bs=512), UNSUP),
+    (dict(dtype=2), UNSUP), (dict(Hq=6, Hkv=4), SHAPE), (dict(Hq=34, Hkv=2), UNSUP),
+    (dict(max_ctx=8 * 16 + 1), SHAPE), (dict(B=-1), SHAPE), (dict(NB=0), SHAPE),
+    (dict(q=Z), NULL), (dict(bt=Z), NULL), (dict(cl=Z), NULL), (dict(out=Z), NULL),
+    (dict(q=MIS), ALIGN), (dict(kc=MIS), ALIGN), (dict(algo=7), ALGO),
+    (dict(algo=2, dtype=0), ALGO), (dict(algo=2, d=64), ALGO), (dict(algo=2, bs=8, MB=16), ALGO),
+    (dict(part=24), SHAPE), (dict(part=-2), SHAPE),
+    (dict(part=32), WS), (dict(part=32, ws=A, wsb=16), WS), (dict(part=-1, max_ctx=1024, MB=64), WS),
+])
+def test_decode_rejects_bad_arguments(lib, kw, status):
+    assert decode_call(lib, **kw) == status
+
+
+@needs_no_gpu
+def test_empty_batch_is_a_no_op(lib):
+    assert decode_call(lib, B=0, q=Z, out=Z) == OK
+    assert lib.pa_reshape_and_cache(Z, Z, Z, Z, Z, 0, 8, 128, 64, 16, 1, Z) == OK
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("args,status", [
+    ((A, A, A, A, A, 4, 8, 48, 64, 16, 1, Z), UNSUP),
+    ((A, A, A, A, A, 4, 8, 128, 64, 3, 1, Z), UNSUP),
+    ((A, A, A, A, A, -1, 8, 128, 64, 16, 1, Z), SHAPE),
+    ((A, A, A, A, A, 4, 0, 128, 64, 16, 1, Z), SHAPE),
+    ((Z, A, A, A, A, 4, 8, 128, 64, 16, 1, Z), NULL),
+    ((A, A, A, A, Z, 4, 8, 128, 64, 16, 1, Z), NULL),
+    ((A, MIS, A, A, A, 4, 8, 128, 64, 16, 1, Z), ALIGN),
+    ((A, A, A, A, A, 4, 8, 128, 64, 16, 5, Z), UNSUP),
+])
+def test_cache_write_rejects_bad_arguments(lib, args, status):
+    assert lib.pa_reshape_and_cache(*args) == status
+
+
+@needs_no_gpu
+def test_reduce_rejects_bad_arguments(lib):
+    assert lib.pa_decode_reduce(A, A, 2, 8, 128, 1000, 0, A, 1 << 20, 1, Z) == SHAPE
+    assert lib.pa_decode_reduce(A, A, 2, 8, 100, 1000, 512, A, 1 << 20, 1, Z) == UNSUP
+    assert lib.pa_decode_reduce(A, A, 2, 8, 128, 1000, 512, A, 16, 1, Z) == WS
+    assert lib.pa_decode_reduce(Z, A, 2, 8, 128, 1000, 512, A, 1 << 20, 1, Z) == NULL
+    assert lib.pa_decode_reduce(A, A, 0, 8, 128, 1000, 512, Z, 0, 1, Z) == OK
