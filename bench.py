@@ -156,9 +156,11 @@ def main():
     max_ctx = int(ctx_h.max())
     out = torch.empty_like(q)
     part_req = c.partition_size if args.partition is None else args.partition
-    part = (pa.pa_decode_auto_partition(c.num_seqs, c.num_kv_heads, c.head_dim, c.block_size,
-                                        max_ctx, pa.dtype_code(q))
+    part = (pa.pa_decode_auto_partition(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                        c.block_size, max_ctx, pa.dtype_code(q))
             if part_req == -1 else part_req)
+    if part == pa.PA_PARTITION_BALANCED and args.algo == "vector":
+        part = 512
     ws = pa.workspace_for(q, k_cache, max_ctx, part)
     torch.cuda.synchronize()
     log(f"workload ready: batch {c.num_seqs}, sum ctx {int(ctx_h.sum())}, partition {part}, "
@@ -183,7 +185,7 @@ def main():
                                     ws, algo, stream=stream)
             if evs is not None:
                 evs[2].record(stream)
-            pa.pa_decode_reduce(out, ctx, max_ctx, part, ws, stream=stream)
+            pa.pa_decode_reduce(out, ctx, c.num_kv_heads, max_ctx, part, ws, stream=stream)
             if evs is not None:
                 evs[3].record(stream)
 

@@ -75,6 +75,11 @@ enum {
     PA_ERR_ALIGN = -7         /* a tensor pointer is not 16-byte aligned          */
 };
 
+/* Special partition_size values for pa_decode / pa_decode_partitions /
+ * pa_decode_reduce / pa_decode_workspace_size. */
+#define PA_PARTITION_AUTO (-1)      /* the library chooses                     */
+#define PA_PARTITION_BALANCED (-2)  /* work-balanced split (matrix-core path)  */
+
 /* Kernel variants for pa_decode / pa_decode_partitions. */
 enum {
     PA_ALGO_AUTO = 0,   /* matrix-core kernel where it applies, else vector    */
@@ -106,17 +111,20 @@ int pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_ca
                          void *stream);
 
 /*
- * Partition size the library uses when pa_decode / pa_decode_partitions get
- * partition_size == -1 for these sizes: 0 (single pass, no workspace) or a
- * multiple of block_size.  A pure function of its arguments.
+ * Partition mode the library uses when pa_decode / pa_decode_partitions get
+ * partition_size == PA_PARTITION_AUTO for these sizes and PA_ALGO_AUTO:
+ * 0 (single pass, no workspace), PA_PARTITION_BALANCED, or a multiple of
+ * block_size.  A pure function of its arguments (with PA_ALGO_VECTOR a
+ * balanced choice becomes 512-token partitions, or single pass when the
+ * context fits one).
  */
-int pa_decode_auto_partition(int num_seqs, int num_kv_heads, int head_dim, int block_size,
-                             int max_context_len, int dtype);
+int pa_decode_auto_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_context_len, int dtype);
 
 /*
  * Bytes of device workspace pa_decode needs (0 in single-pass mode).
- * partition_size as for pa_decode (-1 resolves through
- * pa_decode_auto_partition with these same arguments).  Returns 0 for
+ * partition_size as for pa_decode; for PA_PARTITION_AUTO the size is enough
+ * for every mode the library may pick for these sizes.  Returns 0 for
  * invalid sizes as well.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -143,11 +151,18 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
  *   max_context_len  an upper bound on context_lens (sizes the workspace)
  *   scale         softmax scale (usually 1/sqrt(head_dim))
  *   partition_size   0: single pass, one work unit per (sequence, KV head);
- *                 -1: the library chooses (pa_decode_auto_partition);
+ *                 PA_PARTITION_AUTO: the library chooses
+ *                 (pa_decode_auto_partition);
+ *                 PA_PARTITION_BALANCED: work-balanced split (matrix-core
+ *                 path only): the 16-token tiles of every (KV head,
+ *                 sequence) are laid end to end and a fixed number of
+ *                 wavefronts take equal contiguous shares; pieces of a
+ *                 context cut between wavefronts are merged by log-sum-exp;
  *                 otherwise a multiple of block_size: the context is split
  *                 into partitions of that many tokens, each reduced
  *                 separately, then merged by log-sum-exp (split-context
  *                 decode: pa_decode_partitions followed by pa_decode_reduce).
+ *                 A fixed-partition split may have at most 8192 partitions.
  *   workspace     device scratch of at least pa_decode_workspace_size(...)
  *                 bytes in split mode (ignored in single-pass mode).  Calls
  *                 that share a workspace must be ordered on one stream.
@@ -178,6 +193,8 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
  *     acc [num_seqs][num_q_heads][NP][head_dim]
  * each array starting at a 256-byte aligned offset, in that order.  This is
  * the exchange format for splitting one sequence's context across devices.
+ * With PA_PARTITION_BALANCED the workspace layout is internal to the
+ * library (a plan of the split followed by per-wavefront partial states).
  */
 int pa_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
                          const int32_t *block_tables, const int32_t *context_lens,
@@ -193,9 +210,13 @@ int pa_decode_partitions(void *out, const void *q, const void *k_cache, const vo
  *     M = max_p m_p,  w_p = 2^(m_p - M),
  *     out = (sum_p w_p acc_p) / (sum_p w_p l_p).
  * Sequences with one partition are left alone (phase 1 wrote them).
+ * partition_size must be the value phase 1 resolved (not PA_PARTITION_AUTO;
+ * see pa_decode_auto_partition); with PA_PARTITION_BALANCED the pieces of
+ * each (sequence, KV head) are merged the same way, and empty contexts get
+ * zeros.
  */
 int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int num_q_heads,
-                     int head_dim, int max_context_len, int partition_size,
+                     int num_kv_heads, int head_dim, int max_context_len, int partition_size,
                      const void *workspace, size_t workspace_bytes, int dtype, void *stream);
 
 /* A static, human-readable name for a status code. */

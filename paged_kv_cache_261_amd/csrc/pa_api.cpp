@@ -3,6 +3,7 @@
 // Nothing here allocates device memory or synchronises.
 #include "pa.h"
 
+#include <initializer_list>
 #include <math.h>
 
 #include "pa_internal.h"
@@ -27,23 +28,51 @@ bool dtype_ok(int dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Resolve the partition size: 0 = single pass, else a multiple of block_size.
-int resolve_partition(int partition_size, int num_seqs, int num_kv_heads, int head_dim,
-                      int block_size, int max_context_len, int dtype) {
-    if (partition_size == -1)
-        return pa_decode_auto_partition(num_seqs, num_kv_heads, head_dim, block_size,
-                                        max_context_len, dtype);
-    return partition_size;
+// Wavefronts of the work-balanced split: one per SIMD of an MI355X (256 CUs x
+// 4 SIMDs), all resident at once.  Measured on the bf16 GQA workloads, 1024
+// long streams beat 2048 or more shorter ones.
+#ifndef PA_BALANCED_WAVES
+#define PA_BALANCED_WAVES 1024
+#endif
+constexpr int kBalancedWaves = PA_BALANCED_WAVES;
+
+bool balanced_applies(int dtype, int head_dim, int block_size, int num_q_heads,
+                      int num_kv_heads) {
+    return dtype == PA_BF16 && head_dim == 128 && block_size >= 16 && num_kv_heads > 0 &&
+           num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads <= 16;
+}
+
+// Resolve the partition size: 0 = single pass, PA_PARTITION_BALANCED, or a
+// multiple of block_size.
+int resolve_partition(int partition_size, int num_seqs, int num_q_heads, int num_kv_heads,
+                      int head_dim, int block_size, int max_context_len, int dtype, int algo) {
+    if (partition_size != PA_PARTITION_AUTO) return partition_size;
+    const int p = pa_decode_auto_partition(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           block_size, max_context_len, dtype);
+    if (p == PA_PARTITION_BALANCED && algo == PA_ALGO_VECTOR)
+        return max_context_len > 512 && 512 % block_size == 0 ? 512 : 0;
+    return p;
 }
 
 struct WorkspaceLayout {
-    size_t m_off, l_off, acc_off, total;
+    size_t plan_off, m_off, l_off, acc_off, total;
     int num_partitions;
 };
 
 WorkspaceLayout layout(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
                        int partition) {
     WorkspaceLayout w{};
+    if (partition == PA_PARTITION_BALANCED) {
+        // plan | m [W][2][16] | l [W][2][16] | acc [W][2][16][head_dim]
+        const size_t slots = (size_t)kBalancedWaves * 2 * pa::kMaxGroup;
+        w.num_partitions = 0;
+        w.plan_off = 0;
+        w.m_off = round256((size_t)(pa::kPlanHeader + num_seqs + 1) * sizeof(int32_t));
+        w.l_off = w.m_off + round256(slots * sizeof(float));
+        w.acc_off = w.l_off + round256(slots * sizeof(float));
+        w.total = w.acc_off + round256(slots * head_dim * sizeof(float));
+        return w;
+    }
     w.num_partitions = max_context_len <= 0 ? 1 : (max_context_len + partition - 1) / partition;
     const size_t rows = (size_t)num_seqs * num_q_heads * w.num_partitions;
     w.m_off = 0;
@@ -90,12 +119,14 @@ bool mfma_applies(const DecodeArgs &a) {
 
 // Phase 1 (or the whole decode when num_partitions == 1).
 int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *ws_m,
-                 float *ws_l, float *ws_acc, hipStream_t stream) {
-    const int64_t units = (int64_t)num_partitions * a.num_kv_heads * a.num_seqs;
+                 float *ws_l, float *ws_acc, int *ws_plan, hipStream_t stream) {
+    const bool balanced = partition == PA_PARTITION_BALANCED;
+    const int64_t units =
+        balanced ? kBalancedWaves : (int64_t)num_partitions * a.num_kv_heads * a.num_seqs;
     if (units > 0x7fffffff) return PA_ERR_SHAPE;
     bool use_mfma;
-    if (a.algo == PA_ALGO_MFMA) {
-        if (!mfma_applies(a)) return PA_ERR_ALGO;
+    if (a.algo == PA_ALGO_MFMA || balanced) {
+        if (!mfma_applies(a) || a.algo == PA_ALGO_VECTOR) return PA_ERR_ALGO;
         use_mfma = true;
     } else {
         use_mfma = a.algo == PA_ALGO_AUTO && mfma_applies(a);
@@ -110,6 +141,7 @@ int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *
     p.ws_m = ws_m;
     p.ws_l = ws_l;
     p.ws_acc = ws_acc;
+    p.ws_plan = ws_plan;
     p.num_seqs = a.num_seqs;
     p.num_q_heads = a.num_q_heads;
     p.num_kv_heads = a.num_kv_heads;
@@ -118,10 +150,11 @@ int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *
     p.log2_block = ilog2(a.block_size);
     p.max_blocks_per_seq = a.max_blocks_per_seq;
     p.max_context_len = a.max_context_len;
-    p.partition_size = partition;
+    p.partition_size = balanced ? 0 : partition;
     p.num_partitions = num_partitions;
     p.scale_log2 = a.scale * 1.4426950408889634f;
     p.num_units = (int)units;
+    p.balanced = balanced ? 1 : 0;
     const hipError_t e = use_mfma ? pa::launch_decode_mfma(p, stream)
                                   : pa::launch_decode_vector(p, a.head_dim, a.dtype, stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -162,13 +195,12 @@ int pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_ca
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-int pa_decode_auto_partition(int num_seqs, int num_kv_heads, int head_dim, int block_size,
-                             int max_context_len, int dtype) {
+int pa_decode_auto_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_context_len, int dtype) {
     (void)num_seqs;
-    (void)num_kv_heads;
-    (void)head_dim;
-    (void)dtype;
     if (!block_size_ok(block_size)) return 0;
+    if (balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads))
+        return PA_PARTITION_BALANCED;
     const int partition = block_size > 512 ? block_size : 512;
     return max_context_len > partition ? partition : 0;
 }
@@ -179,9 +211,28 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         max_context_len < 0 || !block_size_ok(block_size))
         return 0;
-    const int partition = resolve_partition(partition_size, num_seqs, num_kv_heads, head_dim,
-                                            block_size, max_context_len, dtype);
-    if (partition <= 0 || partition % block_size) return 0;
+    if (partition_size == PA_PARTITION_AUTO) {
+        // enough for whichever mode pa_decode picks (it may depend on algo)
+        size_t best = 0;
+        const int p = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads,
+                                        head_dim, block_size, max_context_len, dtype,
+                                        PA_ALGO_AUTO);
+        const int pv = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads,
+                                         head_dim, block_size, max_context_len, dtype,
+                                         PA_ALGO_VECTOR);
+        for (int q : {p, pv})
+            if (q == PA_PARTITION_BALANCED || (q > 0 && q % block_size == 0)) {
+                const size_t n = layout(num_seqs, num_q_heads, head_dim, max_context_len, q).total;
+                best = n > best ? n : best;
+            }
+        return best;
+    }
+    const int partition = partition_size;
+    if (partition == PA_PARTITION_BALANCED) {
+        if (!balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads)) return 0;
+    } else if (partition <= 0 || partition % block_size) {
+        return 0;
+    }
     return layout(num_seqs, num_q_heads, head_dim, max_context_len, partition).total;
 }
 
@@ -197,28 +248,38 @@ int pa_decode_partitions(void *out, const void *q, const void *k_cache, const vo
                        max_blocks_per_seq, max_context_len, scale, dtype, algo};
     int rc = validate_decode(a);
     if (rc != PA_OK) return rc;
-    const int partition = resolve_partition(partition_size, num_seqs, num_kv_heads, head_dim,
-                                            block_size, max_context_len, dtype);
-    if (partition <= 0 || partition % block_size) return PA_ERR_SHAPE;
+    const int partition = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads,
+                                            head_dim, block_size, max_context_len, dtype, algo);
+    if (partition == PA_PARTITION_BALANCED) {
+        if (!mfma_applies(a) || algo == PA_ALGO_VECTOR) return PA_ERR_ALGO;
+    } else if (partition <= 0 || partition % block_size) {
+        return PA_ERR_SHAPE;
+    }
     if (num_seqs == 0) return PA_OK;
     const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, max_context_len, partition);
+    if (w.num_partitions > pa::kMaxPartitions) return PA_ERR_SHAPE;
     if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_ALIGN;
     char *ws = (char *)workspace;
     return launch_units(a, partition, w.num_partitions, (float *)(ws + w.m_off),
-                        (float *)(ws + w.l_off), (float *)(ws + w.acc_off), (hipStream_t)stream);
+                        (float *)(ws + w.l_off), (float *)(ws + w.acc_off),
+                        (int *)(ws + w.plan_off), (hipStream_t)stream);
 }
 
 int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int num_q_heads,
-                     int head_dim, int max_context_len, int partition_size,
+                     int num_kv_heads, int head_dim, int max_context_len, int partition_size,
                      const void *workspace, size_t workspace_bytes, int dtype, void *stream) {
-    if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_size <= 0)
+    const bool balanced = partition_size == PA_PARTITION_BALANCED;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+        (partition_size <= 0 && !balanced) || num_q_heads % num_kv_heads)
         return PA_ERR_SHAPE;
     if (!dtype_ok(dtype) || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+    if (balanced && (head_dim != 128 || num_q_heads / num_kv_heads > 16)) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
     if (!out || !context_lens) return PA_ERR_NULL;
     const WorkspaceLayout w =
         layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size);
+    if (w.num_partitions > pa::kMaxPartitions) return PA_ERR_SHAPE;
     if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace) || !aligned16(out)) return PA_ERR_ALIGN;
     const char *ws = (const char *)workspace;
@@ -228,13 +289,19 @@ int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int n
     p.ws_m = (const float *)(ws + w.m_off);
     p.ws_l = (const float *)(ws + w.l_off);
     p.ws_acc = (const float *)(ws + w.acc_off);
+    p.ws_plan = (const int *)(ws + w.plan_off);
     p.num_seqs = num_seqs;
     p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_q_heads / num_kv_heads;
     p.head_dim = head_dim;
     p.max_context_len = max_context_len;
     p.partition_size = partition_size;
     p.num_partitions = w.num_partitions;
-    return pa::launch_reduce(p, dtype, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    const hipError_t e = balanced ? pa::launch_reduce_balanced(p, kBalancedWaves, dtype,
+                                                               (hipStream_t)stream)
+                                  : pa::launch_reduce(p, dtype, (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -247,22 +314,25 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
                        max_blocks_per_seq, max_context_len, scale, dtype, algo};
     int rc = validate_decode(a);
     if (rc != PA_OK) return rc;
-    const int partition = resolve_partition(partition_size, num_seqs, num_kv_heads, head_dim,
-                                            block_size, max_context_len, dtype);
-    if (partition < 0 || (partition > 0 && partition % block_size)) return PA_ERR_SHAPE;
+    const int partition = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads,
+                                            head_dim, block_size, max_context_len, dtype, algo);
+    if (partition != PA_PARTITION_BALANCED &&
+        (partition < 0 || (partition > 0 && partition % block_size)))
+        return PA_ERR_SHAPE;
     if (num_seqs == 0) return PA_OK;
     if (partition == 0) {
         // single pass: one unit per (sequence, KV head) covering the whole context
         const int whole = max_context_len > 0 ? max_context_len : 1;
-        return launch_units(a, whole, 1, nullptr, nullptr, nullptr, (hipStream_t)stream);
+        return launch_units(a, whole, 1, nullptr, nullptr, nullptr, nullptr,
+                            (hipStream_t)stream);
     }
     rc = pa_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                               num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
                               max_blocks_per_seq, max_context_len, scale, partition, workspace,
                               workspace_bytes, dtype, algo, stream);
     if (rc != PA_OK) return rc;
-    return pa_decode_reduce(out, context_lens, num_seqs, num_q_heads, head_dim, max_context_len,
-                            partition, workspace, workspace_bytes, dtype, stream);
+    return pa_decode_reduce(out, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            max_context_len, partition, workspace, workspace_bytes, dtype, stream);
 }
 
 }  // extern "C"

@@ -4,14 +4,13 @@
 // Same result as the vector kernel ("CS349E 第 7 讲 01_paged_attention.py",
 // demo 2, paper eq. 4: scores block by block through the block table, one
 // softmax over the whole context, probability-weighted sum of V), computed
-// one 16-token tile at a time by one wavefront per (sequence, KV head,
-// partition):
+// one 16-token tile at a time by one wavefront:
 //
 //   scores   S[16 tokens x 16 heads] = K_tile[16 x 128] . Q^T[128 x 16]
 //            4 x v_mfma_f32_16x16x32_bf16; the G query heads of the KV head
 //            fill G of the 16 columns (the rest are zero queries);
 //   softmax  online, per head, in base-2 log domain; the tile max is
-//            reduced across the 4 lane groups with two cross-lane shuffles;
+//            reduced across the 4 lane groups with two row-swap permutes;
 //   P.V      O^T[128 x 16] += V_tile^T[128 x 16 tokens] . P^T[16 x 16]
 //            8 x v_mfma_f32_16x16x16_bf16 (P rounded to bfloat16, fp32
 //            accumulation).
@@ -20,23 +19,36 @@
 //  - S: lane holds S[token 4*grp + i][head row16], i = 0..3.  That is
 //    exactly the B operand of the P.V product (k = token 4*grp + i,
 //    column = head row16), so P never leaves the lane.
-//  - K operand (A of the score MFMA, row = token): lane loads the 64
-//    contiguous bytes of token row16 at dims [32*grp, 32*grp + 32); the
+//  - K operand (A of the score MFMA, row = token): for MFMA kk the lane
+//    holds dims [32*kk + 8*grp, +8) of token row16, so each of the four
+//    16-byte loads of a tile reads 64 contiguous bytes of every row; the
 //    query (B, column = head) is loaded with the same dim order, so the
 //    products pair matching dims whatever the hardware's k order is.
 //  - V operand (A of the P.V MFMA, row = dim, k = token): lane loads the 16
-//    contiguous bytes of dims [8*row16, 8*row16 + 8) of tokens 4*grp + i;
-//    MFMA n uses dim 8*row16 + n of those 4 tokens (one byte-permute per
-//    register pair to transpose).
+//    contiguous bytes of dims [8*row16, 8*row16 + 8) of tokens 4*grp + i
+//    (each load reads 4 whole rows); MFMA n uses dim 8*row16 + n of those 4
+//    tokens (one byte-permute per register to transpose).
 //  - O^T accumulator: lane holds head row16 at dims 32*grp + 8*i + n, i.e.
 //    32 contiguous dims, written back as 16-byte stores.
 //
 // Memory: a (block, KV head) tile of 16 tokens x 128 dims is 4 KiB
-// contiguous; each lane issues 4 + 4 sixteen-byte loads per tile, and the
-// next tile's loads are issued before the current tile is computed.  The
-// block table is read 64 entries at a time into one register per lane and
-// each tile's physical block id is taken with a scalar lane read, so the
-// tile base address is computed in scalar registers.
+// contiguous.  Tiles are read through buffer descriptors whose byte range
+// covers only the tile's visible rows, so rows past the context read as
+// zero without a memory access and the tile loop has no branches: the
+// loads of the next tile are issued before the current one is computed and
+// the compiler counts the outstanding loads exactly.  The block-table
+// entry of a tile is read with a scalar load one tile ahead.
+//
+// Two ways to cut the work into wavefronts:
+//  - decode_mfma_kernel: one wavefront per (sequence, KV head, partition of
+//    partition_size tokens) -- single pass when one partition covers the
+//    context, split-context otherwise (merged by reduce_kernel);
+//  - decode_mfma_balanced_kernel: a fixed number W of wavefronts; the tiles
+//    of all (KV head, sequence) units are laid end to end and every
+//    wavefront takes an equal contiguous share of that stream, so the load
+//    is even whatever the mix of context lengths.  A unit that one
+//    wavefront covers whole is finished in place; the pieces of a unit cut
+//    between wavefronts are merged by reduce_balanced_kernel.
 #include "pa_internal.h"
 
 #include <math.h>
@@ -52,9 +64,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kD = 128;          // head_dim handled by this kernel
+constexpr int kD = 128;          // head_dim handled by these kernels
 constexpr int kTile = 16;        // tokens per tile
 constexpr int kRowBytes = kD * 2;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, CDNA
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -96,114 +109,109 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 #endif
 // Occupancy hint: waves per SIMD the register allocation must allow (0: none).
 #ifndef PA_MFMA_WAVES
-#define PA_MFMA_WAVES 0
+#define PA_MFMA_WAVES 3
 #endif
 
 constexpr int kDepth = PA_MFMA_DEPTH;
 constexpr int kBufs = kDepth + 1;
 
-__global__ __launch_bounds__(kWave)
-#if PA_MFMA_WAVES > 0
-__attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES)))
-#endif
-void decode_mfma_kernel(const DecodeParams p) {
-    const int lane = threadIdx.x;
-    const int row16 = lane & 15;
-    const int grp = lane >> 4;
+// Softmax state of one wavefront for the (up to 16) query heads of a unit.
+struct Acc {
+    f32x4 o[8];     // O^T: head row16, dims 32*grp + 8*i + n  ->  o[n][i]
+    float m;        // running max of head row16 (base-2 log domain)
+    float lsum;     // this lane's share of the running sum
+};
 
-    const int u = xcd_remap(blockIdx.x, p.num_units);
-    const Unit w = unit_of(u, p.num_seqs, p.num_kv_heads);
-    const int n = clamp_ctx(p.context_lens[w.b], p.max_context_len);
-    const int P = p.partition_size;
-    const int t0 = w.part * P;
-    const int n_parts = n == 0 ? 1 : (n + P - 1) / P;
-    if (w.part >= n_parts) return;
-    const int t1 = min(n, t0 + P);
-    const int G = p.group;
+struct Lane {
+    int row16, grp;
+};
 
+__device__ __forceinline__ void acc_init(Acc &a) {
+#pragma unroll
+    for (int nn = 0; nn < 8; nn++) a.o[nn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    a.m = -INFINITY;
+    a.lsum = 0.f;
+}
+
+// Query operand of unit (b, g): head row16 of the group, dims
+// [32*kk + 8*grp, +8) for MFMA kk; zero for the padding heads row16 >= G.
+__device__ __forceinline__ void load_q(const DecodeParams &p, int b, int g, Lane ln,
+                                       bf16x8 (&qv)[4]) {
+    const bool real = ln.row16 < p.group;
+    const char *qrow = (const char *)p.q +
+                       (((size_t)b * p.num_q_heads + g * p.group + (real ? ln.row16 : 0)) * kD +
+                        8 * ln.grp) * 2;
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+        u32x4 raw = *(const u32x4 *)(qrow + 64 * kk);
+        if (!real) raw = (u32x4){0u, 0u, 0u, 0u};
+        qv[kk] = __builtin_bit_cast(bf16x8, raw);
+    }
+}
+
+// Tiles [tile_begin, tile_end) of unit (b, g); tile t holds tokens
+// [16 t, 16 t + 16), of which the first n of the sequence are visible.
+__device__ __forceinline__ void run_tiles(const DecodeParams &p, int b, int g, int tile_begin,
+                                          int tile_end, int n, const bf16x8 (&qv)[4], Acc &a,
+                                          Lane ln) {
+    const int ntiles = tile_end - tile_begin;
+    if (ntiles <= 0) return;
     const char *kbase = (const char *)p.k_cache;
     const char *vbase = (const char *)p.v_cache;
-    const int32_t *__restrict__ table = p.block_tables + (size_t)w.b * p.max_blocks_per_seq;
+    const int32_t *__restrict__ table = p.block_tables + (size_t)b * p.max_blocks_per_seq;
     const int log2bs = p.log2_block;
     const int bs_mask = (1 << log2bs) - 1;
+    const int k_lane_off = ln.row16 * kRowBytes + ln.grp * 16;        // + 64 * kk
+    const int v_lane_off = (4 * ln.grp) * kRowBytes + ln.row16 * 16;  // + i * kRowBytes
 
-    // query operand: head row16 of the group, dims [32*grp, 32*grp + 32)
-    bf16x8 qv[4];
-    {
-        const bool real = row16 < G;
-        const char *qrow = (const char *)p.q +
-                           (((size_t)w.b * p.num_q_heads + w.g * G + (real ? row16 : 0)) * kD +
-                            32 * grp) * 2;
-#pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
-            u32x4 raw = *(const u32x4 *)(qrow + 16 * kk);
-            if (!real) raw = (u32x4){0u, 0u, 0u, 0u};
-            qv[kk] = __builtin_bit_cast(bf16x8, raw);
-        }
-    }
-
-    const int k_lane_off = row16 * kRowBytes + grp * 64;       // + 16 * kk
-    const int v_lane_off = (4 * grp) * kRowBytes + row16 * 16; // + i * kRowBytes
-
-    f32x4 o[8];
-#pragma unroll
-    for (int nn = 0; nn < 8; nn++) o[nn] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY;     // running max of head row16 (base-2 log domain)
-    float lsum = 0.f;        // this lane's share of the running sum
-
-    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-
-    // Physical block of tile t (index clamped into the unit, so always a
-    // valid table entry for t >= 0).
+    // Physical block of tile t (t clamped into the range, so the table entry
+    // read always belongs to a visible token).
     auto phys_of = [&](int t) -> int {
-        const int tt = t < ntiles ? t : ntiles - 1;
-        return table[(t0 + tt * kTile) >> log2bs];
+        const int tt = tile_begin + (t < ntiles ? t : ntiles - 1);
+        return table[(tt * kTile) >> log2bs];
     };
-    // Issue the loads of tile t through buffer descriptors whose byte range
-    // covers only the tile's visible token rows: rows past the context (and
-    // every row of a tile past the unit, or of a block id out of range) read
-    // as zero without touching memory, so the loop needs no branches and the
-    // compiler can count outstanding loads exactly.
-    auto load_tile = [&](int t, int phys, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
-        const int tok = t0 + t * kTile;
+    // Issue the loads of tile t; returns its visible row count (0 when the
+    // tile is past the range or its block id is out of range).
+    auto load_tile = [&](int t, int phys, u32x4 (&kr)[4], u32x4 (&vr)[4]) -> int {
+        const int tok = (tile_begin + t) * kTile;
         const bool ok = t < ntiles && (unsigned)phys < (unsigned)p.num_blocks;
-        const int rows = ok ? min(kTile, t1 - tok) : 0;
-        const size_t tile = ((((size_t)(ok ? phys : 0) * p.num_kv_heads + w.g) << log2bs) +
+        const int rows = ok ? min(kTile, n - tok) : 0;
+        const size_t tile = ((((size_t)(ok ? phys : 0) * p.num_kv_heads + g) << log2bs) +
                              (tok & bs_mask)) * (size_t)kRowBytes;
         const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(kbase + tile), (short)0, rows * kRowBytes, 0x00020000);
+            (void *)(kbase + tile), (short)0, rows * kRowBytes, kRsrcWord3);
         const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(vbase + tile), (short)0, rows * kRowBytes, 0x00020000);
+            (void *)(vbase + tile), (short)0, rows * kRowBytes, kRsrcWord3);
 #pragma unroll
-        for (int i = 0; i < 4; i++)   // the 16*i step stays inside the lane's row
+        for (int i = 0; i < 4; i++)   // the 64*i step stays inside the lane's row
             kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  krs, k_lane_off, 16 * i, 0));
+                                                  krs, k_lane_off, 64 * i, 0));
 #pragma unroll
         for (int i = 0; i < 4; i++)
             vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                   vrs, v_lane_off + i * kRowBytes, 0, 0));
+        return rows;
     };
 
-    auto compute_tile = [&](int t, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
+    auto compute_tile = [&](int nv, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
         f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; kk++)
             S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]), qv[kk],
                                                         S, 0, 0, 0);
-        const int nv = t1 - (t0 + t * kTile);     // visible tokens in this tile (>= 1)
         float s[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) s[i] = 4 * grp + i < nv ? S[i] * p.scale_log2 : -INFINITY;
+        for (int i = 0; i < 4; i++) s[i] = 4 * ln.grp + i < nv ? S[i] * p.scale_log2 : -INFINITY;
         const float tmax = xor32_max(xor16_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))));
-        const float m_new = fmaxf(m, tmax);       // finite: the tile has a visible token
-        const float alpha = fast_exp2(m - m_new); // 0 on the first tile (m = -inf)
+        const float m_new = fmaxf(a.m, tmax);       // finite: the tile has a visible row
+        const float alpha = fast_exp2(a.m - m_new); // 0 on the first tile (m = -inf)
         float pr[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) pr[i] = fast_exp2(s[i] - m_new);
-        lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        m = m_new;
+        a.lsum = a.lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        a.m = m_new;
 #pragma unroll
-        for (int nn = 0; nn < 8; nn++) o[nn] *= alpha;
+        for (int nn = 0; nn < 8; nn++) a.o[nn] *= alpha;
         const s16x4 pb = __builtin_bit_cast(
             s16x4, (uint2){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
 #pragma unroll
@@ -213,67 +221,211 @@ void decode_mfma_kernel(const DecodeParams p) {
             const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
             const uint32_t d0 = __builtin_amdgcn_perm(vr[1][nn >> 1], vr[0][nn >> 1], sel);
             const uint32_t d1 = __builtin_amdgcn_perm(vr[3][nn >> 1], vr[2][nn >> 1], sel);
-            const s16x4 a = __builtin_bit_cast(s16x4, (uint2){d0, d1});
-            o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[nn], 0, 0, 0);
+            const s16x4 av = __builtin_bit_cast(s16x4, (uint2){d0, d1});
+            a.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, a.o[nn], 0, 0, 0);
         }
     };
 
-    if (ntiles > 0) {
-        u32x4 kr[kBufs][4], vr[kBufs][4];
-        int phys_next = phys_of(0);
+    u32x4 kr[kBufs][4], vr[kBufs][4];
+    int rows[kBufs];
+    int phys_next = phys_of(0);
 #pragma unroll
-        for (int j = 0; j < kDepth; j++) {         // prologue: tiles 0 .. depth-1
-            load_tile(j, phys_next, kr[j], vr[j]);
-            phys_next = phys_of(j + 1);
+    for (int j = 0; j < kDepth; j++) {         // prologue: tiles 0 .. depth-1
+        rows[j] = load_tile(j, phys_next, kr[j], vr[j]);
+        phys_next = phys_of(j + 1);
+    }
+    for (int tb = 0; tb < ntiles; tb += kBufs) {
+#pragma unroll
+        for (int j = 0; j < kBufs; j++) {
+            const int t = tb + j;
+            if (t >= ntiles) break;
+            const int jn = (j + kDepth) % kBufs;
+            rows[jn] = load_tile(t + kDepth, phys_next, kr[jn], vr[jn]);
+            phys_next = phys_of(t + kDepth + 1);
+            // keep the prefetch ahead of the wait for tile t
+            __builtin_amdgcn_sched_barrier(0);
+            if (rows[j] > 0) compute_tile(rows[j], kr[j], vr[j]);
         }
-        for (int tb = 0; tb < ntiles; tb += kBufs) {
+    }
+}
+
+// Sum the lane shares of l over the 4 lane groups (after the last tile).
+__device__ __forceinline__ void acc_finish(Acc &a) { a.lsum = xor32_sum(xor16_sum(a.lsum)); }
+
+// out[b][g*G + row16] = O / l, in bfloat16.
+__device__ __forceinline__ void store_final(const DecodeParams &p, int b, int g, const Acc &a,
+                                            Lane ln) {
+    if (ln.row16 >= p.group) return;
+    const size_t row = (size_t)b * p.num_q_heads + g * p.group + ln.row16;
+    const float inv = a.lsum > 0.f ? 1.f / a.lsum : 0.f;
+    char *dst = (char *)p.out + (row * kD + 32 * ln.grp) * 2;
 #pragma unroll
-            for (int j = 0; j < kBufs; j++) {
-                const int t = tb + j;
-                if (t >= ntiles) break;
-                load_tile(t + kDepth, phys_next, kr[(j + kDepth) % kBufs], vr[(j + kDepth) % kBufs]);
-                phys_next = phys_of(t + kDepth + 1);
-                // keep the prefetch ahead of the wait for tile t
-                __builtin_amdgcn_sched_barrier(0);
-                compute_tile(t, kr[j], vr[j]);
+    for (int i = 0; i < 4; i++) {
+        u32x4 wv;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            wv[j] = pack_bf16x2(a.o[2 * j][i] * inv, a.o[2 * j + 1][i] * inv);
+        *(u32x4 *)(dst + 16 * i) = wv;
+    }
+}
+
+// Unnormalised partial state of head row16: m and l to m_dst/l_dst, the
+// head's accumulator (head_dim floats) to acc_dst.
+__device__ __forceinline__ void store_partial(float *m_dst, float *l_dst, float *acc_dst,
+                                              const Acc &a, Lane ln) {
+    float *dst = acc_dst + 32 * ln.grp;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const f32x4 lo = {a.o[0][i], a.o[1][i], a.o[2][i], a.o[3][i]};
+        const f32x4 hi = {a.o[4][i], a.o[5][i], a.o[6][i], a.o[7][i]};
+        *(f32x4 *)(dst + 8 * i) = lo;
+        *(f32x4 *)(dst + 8 * i + 4) = hi;
+    }
+    if (ln.grp == 0) {
+        *m_dst = a.m;
+        *l_dst = a.lsum;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One wavefront per (sequence, KV head, partition).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kWave)
+#if PA_MFMA_WAVES > 0
+__attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES)))
+#endif
+void decode_mfma_kernel(const DecodeParams p) {
+    const Lane ln{(int)threadIdx.x & 15, (int)threadIdx.x >> 4};
+    const int u = xcd_remap(blockIdx.x, p.num_units);
+    const Unit w = unit_of(u, p.num_seqs, p.num_kv_heads);
+    const int n = clamp_ctx(p.context_lens[w.b], p.max_context_len);
+    const int P = p.partition_size;
+    const int t0 = w.part * P;
+    const int n_parts = n == 0 ? 1 : (n + P - 1) / P;
+    if (w.part >= n_parts) return;
+    const int t1 = min(n, t0 + P);
+
+    bf16x8 qv[4];
+    load_q(p, w.b, w.g, ln, qv);
+    Acc a;
+    acc_init(a);
+    run_tiles(p, w.b, w.g, t0 / kTile, (t1 + kTile - 1) / kTile, n, qv, a, ln);
+    acc_finish(a);
+    if (n_parts == 1) {
+        store_final(p, w.b, w.g, a, ln);
+    } else if (ln.row16 < p.group) {
+        const size_t prow =
+            ((size_t)w.b * p.num_q_heads + w.g * p.group + ln.row16) * p.num_partitions + w.part;
+        store_partial(p.ws_m + prow, p.ws_l + prow, p.ws_acc + prow * kD, a, ln);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Work-balanced split: W wavefronts share the tile stream evenly.
+//
+// Stream order: KV head g slowest, then sequence b, then tile; sequence b
+// contributes T_b = ceil(n_b / 16) tiles per KV head, so unit (g, b) starts
+// at g * TT + S_b with S_b = sum_{b' < b} T_b' and TT = S_B.  Wavefront w
+// takes [w C, w C + C) with C = ceil(Hkv TT / W).  A wavefront's pieces are
+// whole units (finished in place) except possibly its first and its last;
+// those go to partial slots 0 and 1 of the wavefront.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tiles_of(const DecodeParams &p, int b) {
+    return (clamp_ctx(p.context_lens[b], p.max_context_len) + kTile - 1) / kTile;
+}
+
+__global__ __launch_bounds__(kWave)
+#if PA_MFMA_WAVES > 0
+__attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES)))
+#endif
+void decode_mfma_balanced_kernel(const DecodeParams p) {
+    const int lane = threadIdx.x;
+    const Lane ln{lane & 15, lane >> 4};
+    const int W = p.num_units;
+    const int w = xcd_remap(blockIdx.x, W);
+    const int B = p.num_seqs;
+
+    // tile prefix over sequences: lane i owns sequences [i K, i K + K)
+    const int K = (B + kWave - 1) / kWave;
+    int local = 0;
+    for (int j = 0; j < K; j++) {
+        const int b = lane * K + j;
+        if (b < B) local += tiles_of(p, b);
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    const int excl = incl - local;
+    // values every lane agrees on are moved to scalar registers, so the
+    // compiler treats the unit's addresses as uniform
+    const int TT = __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1));
+    const int total = TT * p.num_kv_heads;
+    const int C = (total + W - 1) / W;
+
+    if (w == 0) {   // the plan, for the merge kernel
+        int s = excl;
+        for (int j = 0; j < K; j++) {
+            const int b = lane * K + j;
+            if (b < B) {
+                p.ws_plan[kPlanHeader + b] = s;
+                s += tiles_of(p, b);
             }
+        }
+        if (lane == 0) {
+            p.ws_plan[0] = W;
+            p.ws_plan[1] = C;
+            p.ws_plan[2] = TT;
         }
     }
 
-    lsum = xor32_sum(xor16_sum(lsum));
-    if (row16 >= G) return;
-    const size_t row = (size_t)w.b * p.num_q_heads + w.g * G + row16;
-    if (n_parts == 1) {
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        char *dst = (char *)p.out + (row * kD + 32 * grp) * 2;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            u32x4 wv;
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                wv[j] = pack_bf16x2(o[2 * j][i] * inv, o[2 * j + 1][i] * inv);
-            *(u32x4 *)(dst + 16 * i) = wv;
+    const int x1 = min(w * C + C, total);
+    int x = w * C;
+    int slot = 0;
+    while (x < x1) {
+        const int g = x / TT;
+        const int r = x - g * TT;
+        // the sequence holding stream position r: find its lane, then walk
+        const unsigned long long own = __ballot(r >= excl && r < incl);
+        const int jl = __builtin_ctzll(own);
+        int base = __builtin_amdgcn_readfirstlane(__shfl(excl, jl));
+        int b = jl * K;
+        int Tb = tiles_of(p, b);
+        while (r >= base + Tb) {
+            base += Tb;
+            b++;
+            Tb = tiles_of(p, b);
         }
-    } else {
-        const size_t prow = row * p.num_partitions + w.part;
-        float *dst = p.ws_acc + prow * kD + 32 * grp;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const f32x4 lo = {o[0][i], o[1][i], o[2][i], o[3][i]};
-            const f32x4 hi = {o[4][i], o[5][i], o[6][i], o[7][i]};
-            *(f32x4 *)(dst + 8 * i) = lo;
-            *(f32x4 *)(dst + 8 * i + 4) = hi;
+        const int t_in = r - base;
+        const int seg = min(Tb - t_in, x1 - x);
+        const int n = clamp_ctx(p.context_lens[b], p.max_context_len);
+
+        bf16x8 qv[4];
+        load_q(p, b, g, ln, qv);
+        Acc a;
+        acc_init(a);
+        run_tiles(p, b, g, t_in, t_in + seg, n, qv, a, ln);
+        acc_finish(a);
+        if (t_in == 0 && seg == Tb) {
+            store_final(p, b, g, a, ln);
+        } else if (ln.row16 < p.group) {
+            const size_t prow = ((size_t)w * 2 + slot) * kMaxGroup + ln.row16;
+            store_partial(p.ws_m + prow, p.ws_l + prow, p.ws_acc + prow * kD, a, ln);
         }
-        if (grp == 0) {
-            p.ws_m[prow] = m;
-            p.ws_l[prow] = lsum;
-        }
+        x += seg;
+        slot = 1;
     }
 }
 
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
     if (p.num_units == 0) return hipSuccess;
-    hipLaunchKernelGGL(decode_mfma_kernel, dim3(p.num_units), dim3(kWave), 0, stream, p);
+    if (p.balanced)
+        hipLaunchKernelGGL(decode_mfma_balanced_kernel, dim3(p.num_units), dim3(kWave), 0, stream,
+                           p);
+    else
+        hipLaunchKernelGGL(decode_mfma_kernel, dim3(p.num_units), dim3(kWave), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libpa.so")
 
 PA_F32, PA_BF16 = 0, 1
 PA_ALGO_AUTO, PA_ALGO_VECTOR, PA_ALGO_MFMA = 0, 1, 2
+PA_PARTITION_AUTO, PA_PARTITION_BALANCED = -1, -2
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALGO", -7: "PA_ERR_ALIGN"}
 
@@ -35,11 +36,11 @@ def _load():
     P, I, F, SZ = C.c_void_p, C.c_int, C.c_float, C.c_size_t
     sig = {
         "pa_reshape_and_cache": (I, [P, P, P, P, P, I, I, I, I, I, I, P]),
-        "pa_decode_auto_partition": (I, [I, I, I, I, I, I]),
+        "pa_decode_auto_partition": (I, [I, I, I, I, I, I, I]),
         "pa_decode_workspace_size": (SZ, [I, I, I, I, I, I, I, I]),
         "pa_decode": (I, [P] * 6 + [I] * 8 + [F, I, P, SZ, I, I, P]),
         "pa_decode_partitions": (I, [P] * 6 + [I] * 8 + [F, I, P, SZ, I, I, P]),
-        "pa_decode_reduce": (I, [P, P, I, I, I, I, I, P, SZ, I, P]),
+        "pa_decode_reduce": (I, [P, P, I, I, I, I, I, I, P, SZ, I, P]),
         "pa_status_string": (C.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
@@ -100,10 +101,10 @@ def pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, stream=None):
            "pa_reshape_and_cache")
 
 
-def pa_decode_auto_partition(num_seqs, num_kv_heads, head_dim, block_size, max_context_len,
-                             dtype=PA_BF16):
-    return lib.pa_decode_auto_partition(num_seqs, num_kv_heads, head_dim, block_size,
-                                        max_context_len, dtype)
+def pa_decode_auto_partition(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_context_len, dtype=PA_BF16):
+    return lib.pa_decode_auto_partition(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        block_size, max_context_len, dtype)
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -162,10 +163,11 @@ def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, s
            "pa_decode_partitions")
 
 
-def pa_decode_reduce(out, context_lens, max_context_len, partition_size, workspace,
+def pa_decode_reduce(out, context_lens, num_kv_heads, max_context_len, partition_size, workspace,
                      stream=None):
     b, hq, d = out.shape
     ws, wsb = _ws(workspace)
-    _check(lib.pa_decode_reduce(_dev(out, "out"), _dev(context_lens, "context_lens"), b, hq, d,
-                                int(max_context_len), int(partition_size), ws, wsb,
-                                dtype_code(out), _stream(out, stream)), "pa_decode_reduce")
+    _check(lib.pa_decode_reduce(_dev(out, "out"), _dev(context_lens, "context_lens"), b, hq,
+                                int(num_kv_heads), d, int(max_context_len), int(partition_size),
+                                ws, wsb, dtype_code(out), _stream(out, stream)),
+           "pa_decode_reduce")

@@ -93,6 +93,7 @@ CONFIGS = {
         name="shared_prefix_bf16", seed=4, num_seqs=256, num_q_heads=32, num_kv_heads=8,
         head_dim=128, block_size=16, num_blocks=16384, max_blocks_per_seq=160, dtype="bf16",
         scale=1 / math.sqrt(128), ctx_rule=("const", 2560), sharing=("fork", 32, 8, 2048),
+        partition_size=0,
         description="bf16 shared-prefix parallel sampling: 32 prompts of 2048 tokens x 8 samples, "
                     "512 private tokens each (ctx 2560), 32 q / 8 kv heads, head_dim 128, block 16"),
     "long_split_bf16": Config(

@@ -143,7 +143,9 @@ def test_full_size_sampled(name):
     ref = pao.decode_concat(q[idx], kh, vh, tab[idx], ctx[idx], w.cfg.scale)
     mc = int(ctx.max())
     bench_part = w.cfg.partition_size        # the launch configuration the benchmark times
-    for algo, part in [(AUTO, bench_part), (MFMA, 0), (MFMA, 512), (VECTOR, 512), (MFMA, 256)]:
+    BAL = pa.PA_PARTITION_BALANCED
+    for algo, part in [(AUTO, bench_part), (AUTO, -1), (MFMA, BAL), (MFMA, 0), (MFMA, 512),
+                       (VECTOR, 512), (MFMA, 256)]:
         note(f"[gpu parity] {name} algo {algo} partition {part}")
         got = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, mc, part, algo)
         H.assert_close_to_oracle(got[idx], ref, "bf16", f"{name} algo {algo} partition {part}")
@@ -192,6 +194,7 @@ def needle_case(dtype, hq, hkv, d, bs, ctxs, c, seed):
 @pytest.mark.parametrize("dtype,algo,hq,hkv,d,bs,part", [
     ("bf16", MFMA, 32, 8, 128, 16, 0), ("bf16", MFMA, 32, 8, 128, 16, 512),
     ("bf16", MFMA, 64, 8, 128, 16, 64), ("bf16", MFMA, 8, 8, 128, 32, 32),
+    ("bf16", MFMA, 32, 8, 128, 16, -2), ("bf16", MFMA, 64, 8, 128, 64, -2),
     ("bf16", VECTOR, 32, 8, 128, 16, 512), ("f32", VECTOR, 8, 8, 64, 16, 0),
     ("f32", VECTOR, 4, 4, 16, 4, 8), ("f32", VECTOR, 12, 4, 32, 1, 0),
 ])
@@ -218,7 +221,7 @@ def test_one_token_and_empty_context(dtype, algo):
     vl = [S._normal(rng, (n, hkv, d), dtype) for n in (1, 1, 5)]
     kc, vc, tab = H.paginate(kl, vl, bs, 8, rng, dtype)
     ctx = np.array([1, 0, 1], dtype=np.int32)
-    for part in (0, 16):
+    for part in ((0, 16, -2) if algo == MFMA else (0, 16)):
         got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, ctx, 0.3, 5, part, algo)
         np.testing.assert_array_equal(got[0], np.repeat(H.to_float(vl[0][0], dtype), 4, axis=0))
         assert (got[1] == 0).all()
@@ -282,7 +285,7 @@ def test_group_sizes_mfma(G):
     vl = [S._normal(rng, (n, 2, 128), "bf16") for n in ctxs]
     kc, vc, tab = H.paginate(kl, vl, 16, 60, rng, "bf16")
     ref = pao.decode_concat(q, kc, vc, tab, np.array(ctxs), 0.09)
-    for part in (0, 128):
+    for part in (0, 128, -2):
         got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, np.array(ctxs), 0.09, None, part,
                            MFMA)
         H.assert_close_to_oracle(got, ref, "bf16", f"G {G} partition {part}")
@@ -329,31 +332,52 @@ def test_physical_placement_and_repeats_do_not_change_bits(dtype, algo):
     kl = [S._normal(rng, (n, 4, 128), dtype) for n in ctxs]
     vl = [S._normal(rng, (n, 4, 128), dtype) for n in ctxs]
     outs = []
+    parts = (0, 512, -2) if algo == MFMA else (0, 512)
     for seed in (10, 11):
         kc, vc, tab = H.paginate(kl, vl, 16, 200, np.random.default_rng(seed), dtype)
         kd, vd = H.to_dev(kc), H.to_dev(vc)
-        for part in (0, 512):
+        for part in parts:
             outs.append((part, H.gpu_decode(q, kd, vd, tab, np.array(ctxs), 0.1, None, part, algo)))
             again = H.gpu_decode(q, kd, vd, tab, np.array(ctxs), 0.1, None, part, algo)
             np.testing.assert_array_equal(outs[-1][1], again)
-    for part in (0, 512):
+    for part in parts:
         a, b = [o for p, o in outs if p == part]
         np.testing.assert_array_equal(a, b)
 
 
-def test_phases_equal_one_call():
+@pytest.mark.parametrize("part", [512, -2])
+def test_phases_equal_one_call(part):
     w, kd, vd, kh, vh = full("long_split_bf16")
     ctx, tab, q = w.ctx_at(0), w.tables_at(0), w.q[0]
     qd, td, cd = H.to_dev(q), H.to_dev(tab), H.to_dev(ctx)
     mc = int(ctx.max())
     out1 = torch.empty_like(qd)
     out2 = torch.empty_like(qd)
-    ws = pa.workspace_for(qd, kd, mc, 512)
-    pa.pa_decode(out1, qd, kd, vd, td, cd, w.cfg.scale, mc, 512, ws)
-    pa.pa_decode_partitions(out2, qd, kd, vd, td, cd, w.cfg.scale, mc, 512, ws)
-    pa.pa_decode_reduce(out2, cd, mc, 512, ws)
+    ws = pa.workspace_for(qd, kd, mc, part)
+    pa.pa_decode(out1, qd, kd, vd, td, cd, w.cfg.scale, mc, part, ws)
+    pa.pa_decode_partitions(out2, qd, kd, vd, td, cd, w.cfg.scale, mc, part, ws)
+    pa.pa_decode_reduce(out2, cd, w.cfg.num_kv_heads, mc, part, ws)
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("ctxs,hkv,G", [([20000, 37], 1, 16), ([1, 2, 3, 40000], 2, 4),
+                                        ([16, 16, 16, 17], 3, 5), ([0, 5000, 0], 1, 8)])
+def test_balanced_split_cuts_anywhere(ctxs, hkv, G):
+    """The balanced split cuts contexts at arbitrary tiles, down to one tile
+    per wavefront; the merged result matches the oracle."""
+    rng = np.random.default_rng(sum(ctxs) + G)
+    hq, d, bs = hkv * G, 128, 16
+    q = S._normal(rng, (len(ctxs), hq, d), "bf16")
+    kl = [S._normal(rng, (n, hkv, d), "bf16") for n in ctxs]
+    vl = [S._normal(rng, (n, hkv, d), "bf16") for n in ctxs]
+    nb = sum((n + bs - 1) // bs for n in ctxs) + 4
+    kc, vc, tab = H.paginate(kl, vl, bs, nb, rng, "bf16")
+    ctx = np.array(ctxs, dtype=np.int32)
+    ref = pao.decode_concat(q, kc, vc, tab, ctx, 1 / math.sqrt(d))
+    got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, ctx, 1 / math.sqrt(d), None,
+                       pa.PA_PARTITION_BALANCED, MFMA)
+    H.assert_close_to_oracle(got, ref, "bf16", f"balanced {ctxs}")
 
 
 def test_copy_on_write_variant_of_shared_prefix():
