@@ -55,7 +55,22 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU work for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the benchmark, copy a 1 GiB buffer with torch 5 times "
+                         "(reference for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device copy of known size, to calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
 def kernel_source_hash():
@@ -116,6 +131,9 @@ def cpu_baseline(w, target_seconds):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"metric": METRIC, "error": "this build measures one GPU only: the "
                           "decode path has no multi-GPU mode; run with --gpus 1"}))

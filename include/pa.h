@@ -194,7 +194,7 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
  * each array starting at a 256-byte aligned offset, in that order.  This is
  * the exchange format for splitting one sequence's context across devices.
  * With PA_PARTITION_BALANCED the workspace layout is internal to the
- * library (a plan of the split followed by per-wavefront partial states).
+ * library (per-wavefront partial states).
  */
 int pa_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
                          const int32_t *block_tables, const int32_t *context_lens,

@@ -55,7 +55,7 @@ int resolve_partition(int partition_size, int num_seqs, int num_q_heads, int num
 }
 
 struct WorkspaceLayout {
-    size_t plan_off, m_off, l_off, acc_off, total;
+    size_t m_off, l_off, acc_off, total;
     int num_partitions;
 };
 
@@ -63,11 +63,10 @@ WorkspaceLayout layout(int num_seqs, int num_q_heads, int head_dim, int max_cont
                        int partition) {
     WorkspaceLayout w{};
     if (partition == PA_PARTITION_BALANCED) {
-        // plan | m [W][2][16] | l [W][2][16] | acc [W][2][16][head_dim]
+        // m [W][2][16] | l [W][2][16] | acc [W][2][16][head_dim]
         const size_t slots = (size_t)kBalancedWaves * 2 * pa::kMaxGroup;
         w.num_partitions = 0;
-        w.plan_off = 0;
-        w.m_off = round256((size_t)(pa::kPlanHeader + num_seqs + 1) * sizeof(int32_t));
+        w.m_off = 0;
         w.l_off = w.m_off + round256(slots * sizeof(float));
         w.acc_off = w.l_off + round256(slots * sizeof(float));
         w.total = w.acc_off + round256(slots * head_dim * sizeof(float));
@@ -119,11 +118,8 @@ bool mfma_applies(const DecodeArgs &a) {
 
 // Phase 1 (or the whole decode when num_partitions == 1).
 int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *ws_m,
-                 float *ws_l, float *ws_acc, int *ws_plan, hipStream_t stream) {
+                 float *ws_l, float *ws_acc, hipStream_t stream) {
     const bool balanced = partition == PA_PARTITION_BALANCED;
-    const int64_t units =
-        balanced ? kBalancedWaves : (int64_t)num_partitions * a.num_kv_heads * a.num_seqs;
-    if (units > 0x7fffffff) return PA_ERR_SHAPE;
     bool use_mfma;
     if (a.algo == PA_ALGO_MFMA || balanced) {
         if (!mfma_applies(a) || a.algo == PA_ALGO_VECTOR) return PA_ERR_ALGO;
@@ -131,6 +127,13 @@ int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *
     } else {
         use_mfma = a.algo == PA_ALGO_AUTO && mfma_applies(a);
     }
+    // Matrix-core path: single pass runs one wavefront per (sequence, KV
+    // head); every split runs the persistent wavefronts.  Vector path: one
+    // wavefront per (sequence, KV head, partition).
+    const bool persistent = use_mfma && num_partitions != 1;
+    const int64_t units = persistent ? kBalancedWaves
+                                     : (int64_t)num_partitions * a.num_kv_heads * a.num_seqs;
+    if (units > 0x7fffffff) return PA_ERR_SHAPE;
     pa::DecodeParams p{};
     p.out = a.out;
     p.q = a.q;
@@ -141,7 +144,6 @@ int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *
     p.ws_m = ws_m;
     p.ws_l = ws_l;
     p.ws_acc = ws_acc;
-    p.ws_plan = ws_plan;
     p.num_seqs = a.num_seqs;
     p.num_q_heads = a.num_q_heads;
     p.num_kv_heads = a.num_kv_heads;
@@ -154,7 +156,7 @@ int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *
     p.num_partitions = num_partitions;
     p.scale_log2 = a.scale * 1.4426950408889634f;
     p.num_units = (int)units;
-    p.balanced = balanced ? 1 : 0;
+    p.persistent = persistent ? 1 : 0;
     const hipError_t e = use_mfma ? pa::launch_decode_mfma(p, stream)
                                   : pa::launch_decode_vector(p, a.head_dim, a.dtype, stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -262,8 +264,7 @@ int pa_decode_partitions(void *out, const void *q, const void *k_cache, const vo
     if (!aligned16(workspace)) return PA_ERR_ALIGN;
     char *ws = (char *)workspace;
     return launch_units(a, partition, w.num_partitions, (float *)(ws + w.m_off),
-                        (float *)(ws + w.l_off), (float *)(ws + w.acc_off),
-                        (int *)(ws + w.plan_off), (hipStream_t)stream);
+                        (float *)(ws + w.l_off), (float *)(ws + w.acc_off), (hipStream_t)stream);
 }
 
 int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int num_q_heads,
@@ -289,7 +290,6 @@ int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int n
     p.ws_m = (const float *)(ws + w.m_off);
     p.ws_l = (const float *)(ws + w.l_off);
     p.ws_acc = (const float *)(ws + w.acc_off);
-    p.ws_plan = (const int *)(ws + w.plan_off);
     p.num_seqs = num_seqs;
     p.num_q_heads = num_q_heads;
     p.num_kv_heads = num_kv_heads;
@@ -298,8 +298,8 @@ int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int n
     p.max_context_len = max_context_len;
     p.partition_size = partition_size;
     p.num_partitions = w.num_partitions;
-    const hipError_t e = balanced ? pa::launch_reduce_balanced(p, kBalancedWaves, dtype,
-                                                               (hipStream_t)stream)
+    p.num_waves = kBalancedWaves;
+    const hipError_t e = balanced ? pa::launch_reduce_balanced(p, dtype, (hipStream_t)stream)
                                   : pa::launch_reduce(p, dtype, (hipStream_t)stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -323,8 +323,7 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
     if (partition == 0) {
         // single pass: one unit per (sequence, KV head) covering the whole context
         const int whole = max_context_len > 0 ? max_context_len : 1;
-        return launch_units(a, whole, 1, nullptr, nullptr, nullptr, nullptr,
-                            (hipStream_t)stream);
+        return launch_units(a, whole, 1, nullptr, nullptr, nullptr, (hipStream_t)stream);
     }
     rc = pa_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                               num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,

@@ -40,15 +40,14 @@
 // entry of a tile is read with a scalar load one tile ahead.
 //
 // Two ways to cut the work into wavefronts:
-//  - decode_mfma_kernel: one wavefront per (sequence, KV head, partition of
-//    partition_size tokens) -- single pass when one partition covers the
-//    context, split-context otherwise (merged by reduce_kernel);
-//  - decode_mfma_balanced_kernel: a fixed number W of wavefronts; the tiles
-//    of all (KV head, sequence) units are laid end to end and every
-//    wavefront takes an equal contiguous share of that stream, so the load
-//    is even whatever the mix of context lengths.  A unit that one
-//    wavefront covers whole is finished in place; the pieces of a unit cut
-//    between wavefronts are merged by reduce_balanced_kernel.
+//  - decode_mfma_kernel: single pass, one wavefront per (sequence, KV head);
+//  - decode_mfma_balanced_kernel: a fixed number W of persistent wavefronts;
+//    the tiles of all (KV head, sequence) units are laid end to end and
+//    every wavefront takes an equal contiguous share of that stream, so the
+//    load is even whatever the mix of context lengths.  Either the shares
+//    are cut at any tile (work-balanced split; pieces merged by
+//    reduce_balanced_kernel) or at partition boundaries (fixed-partition
+//    split; partitions merged by reduce_kernel).
 #include "pa_internal.h"
 
 #include <math.h>
@@ -151,9 +150,14 @@ __device__ __forceinline__ void load_q(const DecodeParams &p, int b, int g, Lane
 
 // Tiles [tile_begin, tile_end) of unit (b, g); tile t holds tokens
 // [16 t, 16 t + 16), of which the first n of the sequence are visible.
+// With emit_every > 0, emit(t) runs after every tile t that ends a run of
+// emit_every tiles (counted from tile 0 of the sequence) and after the last
+// tile; it takes the state of that run and must leave `a` reset.  The loads
+// of the following tiles stay in flight across it.
+template <typename Emit>
 __device__ __forceinline__ void run_tiles(const DecodeParams &p, int b, int g, int tile_begin,
                                           int tile_end, int n, const bf16x8 (&qv)[4], Acc &a,
-                                          Lane ln) {
+                                          Lane ln, int emit_every, Emit &&emit) {
     const int ntiles = tile_end - tile_begin;
     if (ntiles <= 0) return;
     const char *kbase = (const char *)p.k_cache;
@@ -245,9 +249,16 @@ __device__ __forceinline__ void run_tiles(const DecodeParams &p, int b, int g, i
             // keep the prefetch ahead of the wait for tile t
             __builtin_amdgcn_sched_barrier(0);
             if (rows[j] > 0) compute_tile(rows[j], kr[j], vr[j]);
+            if (emit_every > 0 &&
+                ((tile_begin + t + 1) % emit_every == 0 || t == ntiles - 1))
+                emit(tile_begin + t);
         }
     }
 }
+
+struct NoEmit {
+    __device__ void operator()(int) const {}
+};
 
 // Sum the lane shares of l over the 4 lane groups (after the last tile).
 __device__ __forceinline__ void acc_finish(Acc &a) { a.lsum = xor32_sum(xor16_sum(a.lsum)); }
@@ -288,7 +299,10 @@ __device__ __forceinline__ void store_partial(float *m_dst, float *l_dst, float 
 }
 
 // ---------------------------------------------------------------------------
-// One wavefront per (sequence, KV head, partition).
+// Single pass: one wavefront per (sequence, KV head), the whole context.
+// Wavefronts of consecutive sequences with the same KV head run side by
+// side on one XCD, so samples that share prefix blocks read them through
+// the same L2 at about the same time.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kWave)
 #if PA_MFMA_WAVES > 0
@@ -299,51 +313,67 @@ void decode_mfma_kernel(const DecodeParams p) {
     const int u = xcd_remap(blockIdx.x, p.num_units);
     const Unit w = unit_of(u, p.num_seqs, p.num_kv_heads);
     const int n = clamp_ctx(p.context_lens[w.b], p.max_context_len);
-    const int P = p.partition_size;
-    const int t0 = w.part * P;
-    const int n_parts = n == 0 ? 1 : (n + P - 1) / P;
-    if (w.part >= n_parts) return;
-    const int t1 = min(n, t0 + P);
-
     bf16x8 qv[4];
     load_q(p, w.b, w.g, ln, qv);
     Acc a;
     acc_init(a);
-    run_tiles(p, w.b, w.g, t0 / kTile, (t1 + kTile - 1) / kTile, n, qv, a, ln);
+    run_tiles(p, w.b, w.g, 0, (n + kTile - 1) / kTile, n, qv, a, ln, 0, NoEmit{});
     acc_finish(a);
-    if (n_parts == 1) {
-        store_final(p, w.b, w.g, a, ln);
-    } else if (ln.row16 < p.group) {
-        const size_t prow =
-            ((size_t)w.b * p.num_q_heads + w.g * p.group + ln.row16) * p.num_partitions + w.part;
-        store_partial(p.ws_m + prow, p.ws_l + prow, p.ws_acc + prow * kD, a, ln);
-    }
+    store_final(p, w.b, w.g, a, ln);
 }
 
 // ---------------------------------------------------------------------------
-// Work-balanced split: W wavefronts share the tile stream evenly.
+// Persistent split: W wavefronts share the tile stream evenly.
 //
 // Stream order: KV head g slowest, then sequence b, then tile; sequence b
 // contributes T_b = ceil(n_b / 16) tiles per KV head, so unit (g, b) starts
 // at g * TT + S_b with S_b = sum_{b' < b} T_b' and TT = S_B.  Wavefront w
-// takes [w C, w C + C) with C = ceil(Hkv TT / W).  A wavefront's pieces are
-// whole units (finished in place) except possibly its first and its last;
-// those go to partial slots 0 and 1 of the wavefront.
+// owns [w C, w C + C) with C = ceil(Hkv TT / W).
+//
+//  - free cuts (part_tiles == 0, the work-balanced split): the wavefront
+//    computes exactly the tiles it owns.  Its pieces are whole units
+//    (finished in place) except possibly its first and its last, which go
+//    to partial slots 0 and 1 of the wavefront.
+//  - partition cuts (part_tiles == P / 16, fixed partitions of P tokens):
+//    the wavefront computes every partition whose first tile it owns, whole
+//    (so it may run up to one partition past its share), emitting each
+//    partition's state into the [B][Hq][NP] workspace -- or the final output
+//    when the context has one partition.  Consecutive partitions of a unit
+//    keep the tile pipeline running across their boundary.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int tiles_of(const DecodeParams &p, int b) {
     return (clamp_ctx(p.context_lens[b], p.max_context_len) + kTile - 1) / kTile;
+}
+// The same for a sequence index every lane agrees on, as a scalar.
+__device__ __forceinline__ int tiles_of_uniform(const DecodeParams &p, int b) {
+    return __builtin_amdgcn_readfirstlane(tiles_of(p, b));
 }
 
 __global__ __launch_bounds__(kWave)
 #if PA_MFMA_WAVES > 0
 __attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES)))
 #endif
-void decode_mfma_balanced_kernel(const DecodeParams p) {
+void decode_mfma_balanced_kernel(const DecodeParams args, const int32_t *__restrict__ tables,
+                                 const int32_t *__restrict__ ctx_lens, void *__restrict__ out,
+                                 float *__restrict__ ws_m, float *__restrict__ ws_l,
+                                 float *__restrict__ ws_acc) {
+    // The pointers the kernel reads tables through and writes results
+    // through arrive as separate restrict arguments, so the compiler knows
+    // the stores never touch the block tables and keeps the per-tile table
+    // reads on the scalar unit.
+    DecodeParams p = args;
+    p.block_tables = tables;
+    p.context_lens = ctx_lens;
+    p.out = out;
+    p.ws_m = ws_m;
+    p.ws_l = ws_l;
+    p.ws_acc = ws_acc;
     const int lane = threadIdx.x;
     const Lane ln{lane & 15, lane >> 4};
     const int W = p.num_units;
     const int w = xcd_remap(blockIdx.x, W);
     const int B = p.num_seqs;
+    const int PT = p.partition_size / kTile;   // tiles per partition; 0: free cuts
 
     // tile prefix over sequences: lane i owns sequences [i K, i K + K)
     const int K = (B + kWave - 1) / kWave;
@@ -365,22 +395,6 @@ void decode_mfma_balanced_kernel(const DecodeParams p) {
     const int total = TT * p.num_kv_heads;
     const int C = (total + W - 1) / W;
 
-    if (w == 0) {   // the plan, for the merge kernel
-        int s = excl;
-        for (int j = 0; j < K; j++) {
-            const int b = lane * K + j;
-            if (b < B) {
-                p.ws_plan[kPlanHeader + b] = s;
-                s += tiles_of(p, b);
-            }
-        }
-        if (lane == 0) {
-            p.ws_plan[0] = W;
-            p.ws_plan[1] = C;
-            p.ws_plan[2] = TT;
-        }
-    }
-
     const int x1 = min(w * C + C, total);
     int x = w * C;
     int slot = 0;
@@ -392,38 +406,60 @@ void decode_mfma_balanced_kernel(const DecodeParams p) {
         const int jl = __builtin_ctzll(own);
         int base = __builtin_amdgcn_readfirstlane(__shfl(excl, jl));
         int b = jl * K;
-        int Tb = tiles_of(p, b);
+        int Tb = tiles_of_uniform(p, b);
         while (r >= base + Tb) {
             base += Tb;
             b++;
-            Tb = tiles_of(p, b);
+            Tb = tiles_of_uniform(p, b);
         }
-        const int t_in = r - base;
-        const int seg = min(Tb - t_in, x1 - x);
-        const int n = clamp_ctx(p.context_lens[b], p.max_context_len);
+        const int t_in = r - base;                     // first owned tile of the unit
+        const int t_lim = min(Tb, t_in + (x1 - x));    // end of the owned tiles
+        x += t_lim - t_in;
+        int t_begin = t_in, t_end = t_lim;
+        if (PT > 0) {   // the partitions that start inside [t_in, t_lim)
+            t_begin = (t_in + PT - 1) / PT * PT;
+            if (t_begin >= t_lim) continue;
+            t_end = min(Tb, (t_lim - 1) / PT * PT + PT);
+        }
+        const int n = __builtin_amdgcn_readfirstlane(clamp_ctx(p.context_lens[b], p.max_context_len));
 
         bf16x8 qv[4];
         load_q(p, b, g, ln, qv);
         Acc a;
         acc_init(a);
-        run_tiles(p, b, g, t_in, t_in + seg, n, qv, a, ln);
-        acc_finish(a);
-        if (t_in == 0 && seg == Tb) {
-            store_final(p, b, g, a, ln);
-        } else if (ln.row16 < p.group) {
-            const size_t prow = ((size_t)w * 2 + slot) * kMaxGroup + ln.row16;
-            store_partial(p.ws_m + prow, p.ws_l + prow, p.ws_acc + prow * kD, a, ln);
+        if (PT > 0) {
+            const int n_parts = (Tb + PT - 1) / PT;
+            run_tiles(p, b, g, t_begin, t_end, n, qv, a, ln, PT, [&](int t) {
+                acc_finish(a);
+                if (n_parts == 1) {
+                    store_final(p, b, g, a, ln);
+                } else if (ln.row16 < p.group) {
+                    const size_t prow =
+                        ((size_t)b * p.num_q_heads + g * p.group + ln.row16) * p.num_partitions +
+                        t / PT;
+                    store_partial(p.ws_m + prow, p.ws_l + prow, p.ws_acc + prow * kD, a, ln);
+                }
+                acc_init(a);
+            });
+        } else {
+            run_tiles(p, b, g, t_begin, t_end, n, qv, a, ln, 0, NoEmit{});
+            acc_finish(a);
+            if (t_begin == 0 && t_end == Tb) {
+                store_final(p, b, g, a, ln);
+            } else if (ln.row16 < p.group) {
+                const size_t prow = ((size_t)w * 2 + slot) * kMaxGroup + ln.row16;
+                store_partial(p.ws_m + prow, p.ws_l + prow, p.ws_acc + prow * kD, a, ln);
+            }
+            slot = 1;
         }
-        x += seg;
-        slot = 1;
     }
 }
 
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
     if (p.num_units == 0) return hipSuccess;
-    if (p.balanced)
+    if (p.persistent)
         hipLaunchKernelGGL(decode_mfma_balanced_kernel, dim3(p.num_units), dim3(kWave), 0, stream,
-                           p);
+                           p, p.block_tables, p.context_lens, p.out, p.ws_m, p.ws_l, p.ws_acc);
     else
         hipLaunchKernelGGL(decode_mfma_kernel, dim3(p.num_units), dim3(kWave), 0, stream, p);
     return hipGetLastError();

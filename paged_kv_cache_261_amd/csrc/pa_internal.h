@@ -11,9 +11,8 @@ namespace pa {
 constexpr int kWave = 64;   // CDNA wavefront width
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
 
-// Work-balanced split (matrix-core path): plan header length in int32s, and
-// the head slots reserved per partial (the largest supported group).
-constexpr int kPlanHeader = 64;
+// Work-balanced split (matrix-core path): head slots reserved per partial
+// (the largest supported group).
 constexpr int kMaxGroup = 16;
 
 // Everything a decode kernel needs, passed by value as one kernel argument.
@@ -27,7 +26,6 @@ struct DecodeParams {
     float *ws_m;              // [B][Hq][NP]       (split mode only;
     float *ws_l;              // [B][Hq][NP]        balanced mode: [W][2][16],
     float *ws_acc;            // [B][Hq][NP][D]     [W][2][16], [W][2][16][D])
-    int *ws_plan;             // balanced mode: header + per-sequence tile prefix
     int num_seqs;
     int num_q_heads;
     int num_kv_heads;
@@ -39,8 +37,9 @@ struct DecodeParams {
     int partition_size;       // tokens per work unit (single pass: >= max_context_len)
     int num_partitions;       // NP
     float scale_log2;         // scale * log2(e): scores are kept in base-2 log domain
-    int num_units;            // wavefronts: NP * Hkv * B, or W in balanced mode
-    int balanced;             // 1: work-balanced split over num_units wavefronts
+    int num_units;            // wavefronts: NP * Hkv * B (grid), or W (persistent)
+    int persistent;           // matrix-core path: num_units persistent wavefronts share
+                              // the tile stream; partition_size 0 = free cuts
 };
 
 struct ReduceParams {
@@ -49,7 +48,6 @@ struct ReduceParams {
     const float *ws_m;
     const float *ws_l;
     const float *ws_acc;
-    const int *ws_plan;       // balanced mode only
     int num_seqs;
     int num_q_heads;
     int num_kv_heads;
@@ -58,6 +56,7 @@ struct ReduceParams {
     int max_context_len;
     int partition_size;
     int num_partitions;
+    int num_waves;            // balanced mode: wavefronts of the decode kernel
 };
 
 // Work-unit numbering shared by the decode kernels.  Workgroups are handed
@@ -113,8 +112,7 @@ hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 
 hipError_t launch_reduce(const ReduceParams &p, int dtype, hipStream_t stream);
 
-hipError_t launch_reduce_balanced(const ReduceParams &p, int num_waves, int dtype,
-                                  hipStream_t stream);
+hipError_t launch_reduce_balanced(const ReduceParams &p, int dtype, hipStream_t stream);
 
 // Most partitions a fixed-partition split may have (their merge weights sit
 // in the merge kernel's LDS).

@@ -49,8 +49,8 @@ __device__ __forceinline__ float block_max(float x, float *red) {
     return x;
 }
 
-template <int D>
-__device__ __forceinline__ float block_sum(float x, float *red) {
+template <int D, typename V>
+__device__ __forceinline__ V block_sum(V x, V *red) {
     constexpr int kW = D < kWave ? D : kWave;
 #pragma unroll
     for (int o = kW / 2; o >= 1; o >>= 1) x += __shfl_xor(x, o, kW);
@@ -107,9 +107,11 @@ __global__ __launch_bounds__(D) void reduce_kernel(const ReduceParams p) {
 }
 
 // Work-balanced split: one workgroup per (sequence, KV head, head of the
-// group).  The plan left by the decode kernel gives each sequence's first
-// tile S_b in the stream of one KV head, the tiles per KV head TT and the
-// share C of each wavefront.  Unit (g, b) spans stream positions
+// group).  The split is re-derived from the context lengths exactly as the
+// decode kernel made it: sequence b contributes T_b = ceil(n_b / 16) tiles
+// per KV head, S_b = sum_{b' < b} T_b', TT = sum_b T_b, and each of the W
+// wavefronts owned C = ceil(Hkv TT / W) consecutive tiles of the stream
+// (KV head slowest, then sequence, then tile).  Unit (g, b) spans
 // [g TT + S_b, g TT + S_b + T_b); if one wavefront covered it whole, that
 // wavefront wrote the output.  Otherwise wavefronts first..last each hold a
 // piece: wavefront `first` in slot 1 when the unit began inside its share
@@ -122,9 +124,19 @@ __global__ __launch_bounds__(D) void reduce_balanced_kernel(const ReduceParams p
     const int unit = blockIdx.x / p.group;
     const int b = unit / p.num_kv_heads;
     const int g = unit % p.num_kv_heads;
-    const int C = p.ws_plan[1], TT = p.ws_plan[2];
-    const int S = p.ws_plan[kPlanHeader + b];
-    const int Tb = (b + 1 < p.num_seqs ? p.ws_plan[kPlanHeader + b + 1] : TT) - S;
+    constexpr int kTileTokens = 16;
+    int before = 0, all = 0;
+    for (int s = threadIdx.x; s < p.num_seqs; s += D) {
+        const int t = (clamp_ctx(p.context_lens[s], p.max_context_len) + kTileTokens - 1) /
+                      kTileTokens;
+        all += t;
+        if (s < b) before += t;
+    }
+    const int S = block_sum<D>(before, (int *)lds);
+    const int TT = block_sum<D>(all, (int *)lds);
+    const int Tb = (clamp_ctx(p.context_lens[b], p.max_context_len) + kTileTokens - 1) /
+                   kTileTokens;
+    const int C = (TT * p.num_kv_heads + p.num_waves - 1) / p.num_waves;
     T *out = (T *)p.out + ((size_t)b * p.num_q_heads + (size_t)g * p.group + j) * D;
     if (Tb == 0) {
         store_out(out + threadIdx.x, 0.f);
@@ -195,11 +207,10 @@ hipError_t launch_reduce(const ReduceParams &p, int dtype, hipStream_t stream) {
                       : launch_reduce_t<uint16_t>(p, lds, stream);
 }
 
-hipError_t launch_reduce_balanced(const ReduceParams &p, int num_waves, int dtype,
-                                  hipStream_t stream) {
+hipError_t launch_reduce_balanced(const ReduceParams &p, int dtype, hipStream_t stream) {
     const unsigned rows = (unsigned)p.num_seqs * (unsigned)p.num_kv_heads * (unsigned)p.group;
     if (rows == 0) return hipSuccess;
-    const size_t lds = (8 + (size_t)num_waves) * sizeof(float);   // pieces <= wavefronts
+    const size_t lds = (8 + (size_t)p.num_waves) * sizeof(float);   // pieces <= wavefronts
     if (dtype == 0)
         hipLaunchKernelGGL((reduce_balanced_kernel<float, 128>), dim3(rows), dim3(128), lds,
                            stream, p);
