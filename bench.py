@@ -35,8 +35,9 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: achieved KV-read GB/s (% HBM peak) and tokens/s"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "gqa_bf16"
-KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_vector.hip", "pa_reduce.hip",
-                  "pa_cache_write.hip", "pa_api.cpp", "pa_internal.h"]
+KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_shared.hip", "pa_decode_vector.hip",
+                  "pa_reduce.hip", "pa_cache_write.hip", "pa_api.cpp", "pa_internal.h",
+                  "pa_mfma_tile.h"]
 
 
 def log(msg):

@@ -79,6 +79,9 @@ enum {
  * pa_decode_reduce / pa_decode_workspace_size. */
 #define PA_PARTITION_AUTO (-1)      /* the library chooses                     */
 #define PA_PARTITION_BALANCED (-2)  /* work-balanced split (matrix-core path)  */
+#define PA_PARTITION_SHARED (-3)    /* balanced split that reads blocks shared
+                                       by neighbouring sequences once
+                                       (matrix-core path)                      */
 
 /* Kernel variants for pa_decode / pa_decode_partitions. */
 enum {
@@ -158,6 +161,15 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
  *                 sequence) are laid end to end and a fixed number of
  *                 wavefronts take equal contiguous shares; pieces of a
  *                 context cut between wavefronts are merged by log-sum-exp;
+ *                 PA_PARTITION_SHARED: like PA_PARTITION_BALANCED, but
+ *                 consecutive sequences are taken in packs (4 when the
+ *                 group size is at most 4, 2 up to 8, else 1) whose query
+ *                 heads share one wavefront, and a physical block that
+ *                 several members of a pack reference at the same logical
+ *                 position (a shared prefix, e.g. forked samples) is read
+ *                 once for all of them; a planning kernel counts the
+ *                 distinct blocks first so the split stays balanced.  Put
+ *                 sequences that share blocks next to each other;
  *                 otherwise a multiple of block_size: the context is split
  *                 into partitions of that many tokens, each reduced
  *                 separately, then merged by log-sum-exp (split-context
@@ -193,8 +205,8 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
  *     acc [num_seqs][num_q_heads][NP][head_dim]
  * each array starting at a 256-byte aligned offset, in that order.  This is
  * the exchange format for splitting one sequence's context across devices.
- * With PA_PARTITION_BALANCED the workspace layout is internal to the
- * library (per-wavefront partial states).
+ * With PA_PARTITION_BALANCED or PA_PARTITION_SHARED the workspace layout is
+ * internal to the library (a plan and per-wavefront partial states).
  */
 int pa_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
                          const int32_t *block_tables, const int32_t *context_lens,

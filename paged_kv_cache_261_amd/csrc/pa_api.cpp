@@ -35,6 +35,18 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 #define PA_BALANCED_WAVES 1024
 #endif
 constexpr int kBalancedWaves = PA_BALANCED_WAVES;
+#ifndef PA_SHARED_WAVES
+#define PA_SHARED_WAVES 1024
+#endif
+constexpr int kSharedWaves = PA_SHARED_WAVES;
+
+// Sequences per pack in shared-prefix mode: as many as fit the 16 columns,
+// at most 4.
+int pack_of(int group) { return group <= 4 ? 4 : (group <= 8 ? 2 : 1); }
+
+bool is_split_mode(int partition) {
+    return partition == PA_PARTITION_BALANCED || partition == PA_PARTITION_SHARED;
+}
 
 bool balanced_applies(int dtype, int head_dim, int block_size, int num_q_heads,
                       int num_kv_heads) {
@@ -56,12 +68,31 @@ int resolve_partition(int partition_size, int num_seqs, int num_q_heads, int num
 
 struct WorkspaceLayout {
     size_t m_off, l_off, acc_off, total;
+    size_t cost_off, pos_off, dir_off;   // shared-prefix mode
     int num_partitions;
+    int pack, num_packs, max_tiles;      // shared-prefix mode
 };
 
 WorkspaceLayout layout(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
-                       int partition) {
+                       int partition, int group = 1) {
     WorkspaceLayout w{};
+    if (partition == PA_PARTITION_SHARED) {
+        // cost [P] | pos [P][max_tiles + 1] | dir [W][2] | m, l [W][2][16] |
+        // acc [W][2][16][head_dim]
+        const size_t slots = (size_t)kSharedWaves * 2 * pa::kMaxGroup;
+        w.pack = pack_of(group);
+        w.num_packs = (num_seqs + w.pack - 1) / w.pack;
+        w.max_tiles = (max_context_len + 15) / 16;
+        w.cost_off = 0;
+        w.pos_off = round256((size_t)w.num_packs * sizeof(int32_t));
+        w.dir_off = w.pos_off +
+                    round256((size_t)w.num_packs * (w.max_tiles + 1) * sizeof(int32_t));
+        w.m_off = w.dir_off + round256((size_t)kSharedWaves * 2 * sizeof(int32_t));
+        w.l_off = w.m_off + round256(slots * sizeof(float));
+        w.acc_off = w.l_off + round256(slots * sizeof(float));
+        w.total = w.acc_off + round256(slots * head_dim * sizeof(float));
+        return w;
+    }
     if (partition == PA_PARTITION_BALANCED) {
         // m [W][2][16] | l [W][2][16] | acc [W][2][16][head_dim]
         const size_t slots = (size_t)kBalancedWaves * 2 * pa::kMaxGroup;
@@ -162,6 +193,36 @@ int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+pa::SharedParams shared_params(const DecodeArgs &a, const WorkspaceLayout &w, char *ws) {
+    pa::SharedParams p{};
+    p.out = a.out;
+    p.q = a.q;
+    p.k_cache = a.k_cache;
+    p.v_cache = a.v_cache;
+    p.block_tables = a.block_tables;
+    p.context_lens = a.context_lens;
+    p.num_seqs = a.num_seqs;
+    p.num_q_heads = a.num_q_heads;
+    p.num_kv_heads = a.num_kv_heads;
+    p.group = a.num_q_heads / a.num_kv_heads;
+    p.num_blocks = a.num_blocks;
+    p.log2_block = ilog2(a.block_size);
+    p.max_blocks_per_seq = a.max_blocks_per_seq;
+    p.max_context_len = a.max_context_len;
+    p.scale_log2 = a.scale * 1.4426950408889634f;
+    p.pack = w.pack;
+    p.num_packs = w.num_packs;
+    p.max_tiles = w.max_tiles;
+    p.num_waves = kSharedWaves;
+    p.ws_cost = (int *)(ws + w.cost_off);
+    p.ws_pos = (int *)(ws + w.pos_off);
+    p.ws_dir = (int *)(ws + w.dir_off);
+    p.ws_m = (float *)(ws + w.m_off);
+    p.ws_l = (float *)(ws + w.l_off);
+    p.ws_acc = (float *)(ws + w.acc_off);
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,19 +284,21 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                          head_dim, block_size, max_context_len, dtype,
                                          PA_ALGO_VECTOR);
         for (int q : {p, pv})
-            if (q == PA_PARTITION_BALANCED || (q > 0 && q % block_size == 0)) {
+            if (is_split_mode(q) || (q > 0 && q % block_size == 0)) {
                 const size_t n = layout(num_seqs, num_q_heads, head_dim, max_context_len, q).total;
                 best = n > best ? n : best;
             }
         return best;
     }
     const int partition = partition_size;
-    if (partition == PA_PARTITION_BALANCED) {
+    if (is_split_mode(partition)) {
         if (!balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads)) return 0;
     } else if (partition <= 0 || partition % block_size) {
         return 0;
     }
-    return layout(num_seqs, num_q_heads, head_dim, max_context_len, partition).total;
+    return layout(num_seqs, num_q_heads, head_dim, max_context_len, partition,
+                  num_q_heads / num_kv_heads)
+        .total;
 }
 
 int pa_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -252,17 +315,23 @@ int pa_decode_partitions(void *out, const void *q, const void *k_cache, const vo
     if (rc != PA_OK) return rc;
     const int partition = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads,
                                             head_dim, block_size, max_context_len, dtype, algo);
-    if (partition == PA_PARTITION_BALANCED) {
+    if (is_split_mode(partition)) {
         if (!mfma_applies(a) || algo == PA_ALGO_VECTOR) return PA_ERR_ALGO;
     } else if (partition <= 0 || partition % block_size) {
         return PA_ERR_SHAPE;
     }
     if (num_seqs == 0) return PA_OK;
-    const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, max_context_len, partition);
+    const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, max_context_len, partition,
+                                     num_q_heads / num_kv_heads);
     if (w.num_partitions > pa::kMaxPartitions) return PA_ERR_SHAPE;
     if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_ALIGN;
     char *ws = (char *)workspace;
+    if (partition == PA_PARTITION_SHARED) {
+        const hipError_t e =
+            pa::launch_decode_shared(shared_params(a, w, ws), 1, (hipStream_t)stream);
+        return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    }
     return launch_units(a, partition, w.num_partitions, (float *)(ws + w.m_off),
                         (float *)(ws + w.l_off), (float *)(ws + w.acc_off), (hipStream_t)stream);
 }
@@ -270,20 +339,35 @@ int pa_decode_partitions(void *out, const void *q, const void *k_cache, const vo
 int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int num_q_heads,
                      int num_kv_heads, int head_dim, int max_context_len, int partition_size,
                      const void *workspace, size_t workspace_bytes, int dtype, void *stream) {
-    const bool balanced = partition_size == PA_PARTITION_BALANCED;
+    const bool balanced = is_split_mode(partition_size);
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
         (partition_size <= 0 && !balanced) || num_q_heads % num_kv_heads)
         return PA_ERR_SHAPE;
     if (!dtype_ok(dtype) || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
-    if (balanced && (head_dim != 128 || num_q_heads / num_kv_heads > 16)) return PA_ERR_UNSUPPORTED;
+    if (balanced && (head_dim != 128 || dtype != PA_BF16 || num_q_heads / num_kv_heads > 16))
+        return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
     if (!out || !context_lens) return PA_ERR_NULL;
-    const WorkspaceLayout w =
-        layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size);
+    const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, max_context_len,
+                                     partition_size, num_q_heads / num_kv_heads);
     if (w.num_partitions > pa::kMaxPartitions) return PA_ERR_SHAPE;
     if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace) || !aligned16(out)) return PA_ERR_ALIGN;
     const char *ws = (const char *)workspace;
+    if (partition_size == PA_PARTITION_SHARED) {
+        DecodeArgs a{};
+        a.out = out;
+        a.context_lens = context_lens;
+        a.num_seqs = num_seqs;
+        a.num_q_heads = num_q_heads;
+        a.num_kv_heads = num_kv_heads;
+        a.head_dim = head_dim;
+        a.block_size = 16;
+        a.max_context_len = max_context_len;
+        const hipError_t e = pa::launch_decode_shared(shared_params(a, w, (char *)ws), 2,
+                                                      (hipStream_t)stream);
+        return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    }
     pa::ReduceParams p{};
     p.out = out;
     p.context_lens = context_lens;
@@ -316,8 +400,7 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
     if (rc != PA_OK) return rc;
     const int partition = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads,
                                             head_dim, block_size, max_context_len, dtype, algo);
-    if (partition != PA_PARTITION_BALANCED &&
-        (partition < 0 || (partition > 0 && partition % block_size)))
+    if (!is_split_mode(partition) && (partition < 0 || (partition > 0 && partition % block_size)))
         return PA_ERR_SHAPE;
     if (num_seqs == 0) return PA_OK;
     if (partition == 0) {

@@ -4,32 +4,9 @@
 // Same result as the vector kernel ("CS349E 第 7 讲 01_paged_attention.py",
 // demo 2, paper eq. 4: scores block by block through the block table, one
 // softmax over the whole context, probability-weighted sum of V), computed
-// one 16-token tile at a time by one wavefront:
-//
-//   scores   S[16 tokens x 16 heads] = K_tile[16 x 128] . Q^T[128 x 16]
-//            4 x v_mfma_f32_16x16x32_bf16; the G query heads of the KV head
-//            fill G of the 16 columns (the rest are zero queries);
-//   softmax  online, per head, in base-2 log domain; the tile max is
-//            reduced across the 4 lane groups with two row-swap permutes;
-//   P.V      O^T[128 x 16] += V_tile^T[128 x 16 tokens] . P^T[16 x 16]
-//            8 x v_mfma_f32_16x16x16_bf16 (P rounded to bfloat16, fp32
-//            accumulation).
-//
-// Register layouts (lane = 16 * grp + row16):
-//  - S: lane holds S[token 4*grp + i][head row16], i = 0..3.  That is
-//    exactly the B operand of the P.V product (k = token 4*grp + i,
-//    column = head row16), so P never leaves the lane.
-//  - K operand (A of the score MFMA, row = token): for MFMA kk the lane
-//    holds dims [32*kk + 8*grp, +8) of token row16, so each of the four
-//    16-byte loads of a tile reads 64 contiguous bytes of every row; the
-//    query (B, column = head) is loaded with the same dim order, so the
-//    products pair matching dims whatever the hardware's k order is.
-//  - V operand (A of the P.V MFMA, row = dim, k = token): lane loads the 16
-//    contiguous bytes of dims [8*row16, 8*row16 + 8) of tokens 4*grp + i
-//    (each load reads 4 whole rows); MFMA n uses dim 8*row16 + n of those 4
-//    tokens (one byte-permute per register to transpose).
-//  - O^T accumulator: lane holds head row16 at dims 32*grp + 8*i + n, i.e.
-//    32 contiguous dims, written back as 16-byte stores.
+// one 16-token tile at a time by one wavefront whose 16 MFMA columns hold the
+// G query heads of one KV head (the rest are zero queries); the per-tile step
+// and its register layouts are in pa_mfma_tile.h.
 //
 // Memory: a (block, KV head) tile of 16 tokens x 128 dims is 4 KiB
 // contiguous.  Tiles are read through buffer descriptors whose byte range
@@ -48,59 +25,11 @@
 //    are cut at any tile (work-balanced split; pieces merged by
 //    reduce_balanced_kernel) or at partition boundaries (fixed-partition
 //    split; partitions merged by reduce_kernel).
-#include "pa_internal.h"
+#include "pa_mfma_tile.h"
 
 #include <math.h>
 
 namespace pa {
-
-namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kD = 128;          // head_dim handled by these kernels
-constexpr int kTile = 16;        // tokens per tile
-constexpr int kRowBytes = kD * 2;
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, CDNA
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// max / sum with the lane 16 (resp. 32) positions away, on the VALU: the
-// gfx950 row-swap permutes exchange rows of 16 lanes (resp. halves of the
-// wave) between two registers, so swapping a value with itself pairs every
-// lane with lane ^ 16 (resp. lane ^ 32).
-__device__ __forceinline__ float xor16_max(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_max(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor16_sum(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    const f32x2 f = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));   // RNE
-}
-
-}  // namespace
 
 // Prefetch depth: tiles whose loads are in flight while a tile is computed.
 #ifndef PA_MFMA_DEPTH
@@ -113,24 +42,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 constexpr int kDepth = PA_MFMA_DEPTH;
 constexpr int kBufs = kDepth + 1;
-
-// Softmax state of one wavefront for the (up to 16) query heads of a unit.
-struct Acc {
-    f32x4 o[8];     // O^T: head row16, dims 32*grp + 8*i + n  ->  o[n][i]
-    float m;        // running max of head row16 (base-2 log domain)
-    float lsum;     // this lane's share of the running sum
-};
-
-struct Lane {
-    int row16, grp;
-};
-
-__device__ __forceinline__ void acc_init(Acc &a) {
-#pragma unroll
-    for (int nn = 0; nn < 8; nn++) a.o[nn] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    a.m = -INFINITY;
-    a.lsum = 0.f;
-}
 
 // Query operand of unit (b, g): head row16 of the group, dims
 // [32*kk + 8*grp, +8) for MFMA kk; zero for the padding heads row16 >= G.
@@ -165,9 +76,6 @@ __device__ __forceinline__ void run_tiles(const DecodeParams &p, int b, int g, i
     const int32_t *__restrict__ table = p.block_tables + (size_t)b * p.max_blocks_per_seq;
     const int log2bs = p.log2_block;
     const int bs_mask = (1 << log2bs) - 1;
-    const int k_lane_off = ln.row16 * kRowBytes + ln.grp * 16;        // + 64 * kk
-    const int v_lane_off = (4 * ln.grp) * kRowBytes + ln.row16 * 16;  // + i * kRowBytes
-
     // Physical block of tile t (t clamped into the range, so the table entry
     // read always belongs to a visible token).
     auto phys_of = [&](int t) -> int {
@@ -182,52 +90,8 @@ __device__ __forceinline__ void run_tiles(const DecodeParams &p, int b, int g, i
         const int rows = ok ? min(kTile, n - tok) : 0;
         const size_t tile = ((((size_t)(ok ? phys : 0) * p.num_kv_heads + g) << log2bs) +
                              (tok & bs_mask)) * (size_t)kRowBytes;
-        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(kbase + tile), (short)0, rows * kRowBytes, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(vbase + tile), (short)0, rows * kRowBytes, kRsrcWord3);
-#pragma unroll
-        for (int i = 0; i < 4; i++)   // the 64*i step stays inside the lane's row
-            kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  krs, k_lane_off, 64 * i, 0));
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  vrs, v_lane_off + i * kRowBytes, 0, 0));
+        load_tile_rows(kbase, vbase, tile, rows, ln, kr, vr);
         return rows;
-    };
-
-    auto compute_tile = [&](int nv, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
-        f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; kk++)
-            S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]), qv[kk],
-                                                        S, 0, 0, 0);
-        float s[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) s[i] = 4 * ln.grp + i < nv ? S[i] * p.scale_log2 : -INFINITY;
-        const float tmax = xor32_max(xor16_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))));
-        const float m_new = fmaxf(a.m, tmax);       // finite: the tile has a visible row
-        const float alpha = fast_exp2(a.m - m_new); // 0 on the first tile (m = -inf)
-        float pr[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) pr[i] = fast_exp2(s[i] - m_new);
-        a.lsum = a.lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        a.m = m_new;
-#pragma unroll
-        for (int nn = 0; nn < 8; nn++) a.o[nn] *= alpha;
-        const s16x4 pb = __builtin_bit_cast(
-            s16x4, (uint2){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
-#pragma unroll
-        for (int nn = 0; nn < 8; nn++) {
-            // dim 8*row16 + nn of tokens 4*grp + 0..3: word nn/2 of each row,
-            // low half for even nn, high half for odd nn
-            const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t d0 = __builtin_amdgcn_perm(vr[1][nn >> 1], vr[0][nn >> 1], sel);
-            const uint32_t d1 = __builtin_amdgcn_perm(vr[3][nn >> 1], vr[2][nn >> 1], sel);
-            const s16x4 av = __builtin_bit_cast(s16x4, (uint2){d0, d1});
-            a.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, a.o[nn], 0, 0, 0);
-        }
     };
 
     u32x4 kr[kBufs][4], vr[kBufs][4];
@@ -248,7 +112,7 @@ __device__ __forceinline__ void run_tiles(const DecodeParams &p, int b, int g, i
             phys_next = phys_of(t + kDepth + 1);
             // keep the prefetch ahead of the wait for tile t
             __builtin_amdgcn_sched_barrier(0);
-            if (rows[j] > 0) compute_tile(rows[j], kr[j], vr[j]);
+            if (rows[j] > 0) tile_update<false>(kr[j], vr[j], qv, rows[j], p.scale_log2, a, ln);
             if (emit_every > 0 &&
                 ((tile_begin + t + 1) % emit_every == 0 || t == ntiles - 1))
                 emit(tile_begin + t);
@@ -260,42 +124,13 @@ struct NoEmit {
     __device__ void operator()(int) const {}
 };
 
-// Sum the lane shares of l over the 4 lane groups (after the last tile).
-__device__ __forceinline__ void acc_finish(Acc &a) { a.lsum = xor32_sum(xor16_sum(a.lsum)); }
 
 // out[b][g*G + row16] = O / l, in bfloat16.
 __device__ __forceinline__ void store_final(const DecodeParams &p, int b, int g, const Acc &a,
                                             Lane ln) {
     if (ln.row16 >= p.group) return;
-    const size_t row = (size_t)b * p.num_q_heads + g * p.group + ln.row16;
-    const float inv = a.lsum > 0.f ? 1.f / a.lsum : 0.f;
-    char *dst = (char *)p.out + (row * kD + 32 * ln.grp) * 2;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        u32x4 wv;
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            wv[j] = pack_bf16x2(a.o[2 * j][i] * inv, a.o[2 * j + 1][i] * inv);
-        *(u32x4 *)(dst + 16 * i) = wv;
-    }
-}
-
-// Unnormalised partial state of head row16: m and l to m_dst/l_dst, the
-// head's accumulator (head_dim floats) to acc_dst.
-__device__ __forceinline__ void store_partial(float *m_dst, float *l_dst, float *acc_dst,
-                                              const Acc &a, Lane ln) {
-    float *dst = acc_dst + 32 * ln.grp;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const f32x4 lo = {a.o[0][i], a.o[1][i], a.o[2][i], a.o[3][i]};
-        const f32x4 hi = {a.o[4][i], a.o[5][i], a.o[6][i], a.o[7][i]};
-        *(f32x4 *)(dst + 8 * i) = lo;
-        *(f32x4 *)(dst + 8 * i + 4) = hi;
-    }
-    if (ln.grp == 0) {
-        *m_dst = a.m;
-        *l_dst = a.lsum;
-    }
+    store_row((char *)p.out + ((size_t)b * p.num_q_heads + g * p.group + ln.row16) * kD * 2, a,
+              ln);
 }
 
 // ---------------------------------------------------------------------------

@@ -59,6 +59,36 @@ struct ReduceParams {
     int num_waves;            // balanced mode: wavefronts of the decode kernel
 };
 
+// Shared-prefix decode (matrix-core path): packs of `pack` consecutive
+// sequences share one wavefront's 16 columns.
+struct SharedParams {
+    void *out;
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int group;
+    int num_blocks;
+    int log2_block;
+    int max_blocks_per_seq;
+    int max_context_len;
+    float scale_log2;
+    int pack;                 // sequences per pack
+    int num_packs;            // ceil(num_seqs / pack)
+    int max_tiles;            // ceil(max_context_len / 16); pos rows hold max_tiles + 1
+    int num_waves;            // persistent wavefronts
+    int *ws_cost;             // [num_packs] distinct tiles per pack
+    int *ws_pos;              // [num_packs][max_tiles + 1] cost before each tile index
+    int *ws_dir;              // [W][2] pack unit held by each partial slot, or -1
+    float *ws_m;              // [W][2][16]
+    float *ws_l;              // [W][2][16]
+    float *ws_acc;            // [W][2][16][128]
+};
+
 // Work-unit numbering shared by the decode kernels.  Workgroups are handed
 // to the 8 XCDs round-robin (workgroup w runs on XCD w % 8); this remaps the
 // workgroup id so that consecutive logical units run on the same XCD at about
@@ -113,6 +143,9 @@ hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams &p, int dtype, hipStream_t stream);
 
 hipError_t launch_reduce_balanced(const ReduceParams &p, int dtype, hipStream_t stream);
+
+// phase bit 1: plan + decode kernels; bit 2: merge kernel.
+hipError_t launch_decode_shared(const SharedParams &p, int phase, hipStream_t stream);
 
 // Most partitions a fixed-partition split may have (their merge weights sit
 // in the merge kernel's LDS).

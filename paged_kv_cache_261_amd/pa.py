@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libpa.so")
 
 PA_F32, PA_BF16 = 0, 1
 PA_ALGO_AUTO, PA_ALGO_VECTOR, PA_ALGO_MFMA = 0, 1, 2
-PA_PARTITION_AUTO, PA_PARTITION_BALANCED = -1, -2
+PA_PARTITION_AUTO, PA_PARTITION_BALANCED, PA_PARTITION_SHARED = -1, -2, -3
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALGO", -7: "PA_ERR_ALIGN"}
 

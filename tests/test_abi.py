@@ -104,7 +104,8 @@ def decode_call(lib, fn="pa_decode", **kw):
     (dict(q=Z), NULL), (dict(bt=Z), NULL), (dict(cl=Z), NULL), (dict(out=Z), NULL),
     (dict(q=MIS), ALIGN), (dict(kc=MIS), ALIGN), (dict(algo=7), ALGO),
     (dict(algo=2, dtype=0), ALGO), (dict(algo=2, d=64), ALGO), (dict(algo=2, bs=8, MB=16), ALGO),
-    (dict(part=24), SHAPE), (dict(part=-3), SHAPE), (dict(part=-2, dtype=0, d=64), ALGO),
+    (dict(part=24), SHAPE), (dict(part=-4), SHAPE), (dict(part=-2, dtype=0, d=64), ALGO),
+    (dict(part=-3, dtype=0), ALGO), (dict(part=-3, algo=1), ALGO), (dict(part=-3), WS),
     (dict(part=-2, algo=1), ALGO), (dict(part=-2), WS),
     (dict(part=32), WS), (dict(part=32, ws=A, wsb=16), WS), (dict(part=-1, max_ctx=1024, MB=64), WS),
 ])

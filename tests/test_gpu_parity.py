@@ -143,9 +143,9 @@ def test_full_size_sampled(name):
     ref = pao.decode_concat(q[idx], kh, vh, tab[idx], ctx[idx], w.cfg.scale)
     mc = int(ctx.max())
     bench_part = w.cfg.partition_size        # the launch configuration the benchmark times
-    BAL = pa.PA_PARTITION_BALANCED
-    for algo, part in [(AUTO, bench_part), (AUTO, -1), (MFMA, BAL), (MFMA, 0), (MFMA, 512),
-                       (VECTOR, 512), (MFMA, 256)]:
+    BAL, SHR = pa.PA_PARTITION_BALANCED, pa.PA_PARTITION_SHARED
+    for algo, part in [(AUTO, bench_part), (AUTO, -1), (MFMA, BAL), (MFMA, SHR), (MFMA, 0),
+                       (MFMA, 512), (VECTOR, 512), (MFMA, 256)]:
         note(f"[gpu parity] {name} algo {algo} partition {part}")
         got = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, mc, part, algo)
         H.assert_close_to_oracle(got[idx], ref, "bf16", f"{name} algo {algo} partition {part}")
@@ -195,7 +195,8 @@ def needle_case(dtype, hq, hkv, d, bs, ctxs, c, seed):
     ("bf16", MFMA, 32, 8, 128, 16, 0), ("bf16", MFMA, 32, 8, 128, 16, 512),
     ("bf16", MFMA, 64, 8, 128, 16, 64), ("bf16", MFMA, 8, 8, 128, 32, 32),
     ("bf16", MFMA, 32, 8, 128, 16, -2), ("bf16", MFMA, 64, 8, 128, 64, -2),
-    ("bf16", VECTOR, 32, 8, 128, 16, 512), ("f32", VECTOR, 8, 8, 64, 16, 0),
+    ("bf16", MFMA, 32, 8, 128, 16, -3), ("bf16", MFMA, 64, 8, 128, 64, -3),
+    ("bf16", MFMA, 16, 16, 128, 32, -3), ("bf16", VECTOR, 32, 8, 128, 16, 512), ("f32", VECTOR, 8, 8, 64, 16, 0),
     ("f32", VECTOR, 4, 4, 16, 4, 8), ("f32", VECTOR, 12, 4, 32, 1, 0),
 ])
 def test_needle_is_bit_exact(dtype, algo, hq, hkv, d, bs, part):
@@ -221,7 +222,7 @@ def test_one_token_and_empty_context(dtype, algo):
     vl = [S._normal(rng, (n, hkv, d), dtype) for n in (1, 1, 5)]
     kc, vc, tab = H.paginate(kl, vl, bs, 8, rng, dtype)
     ctx = np.array([1, 0, 1], dtype=np.int32)
-    for part in ((0, 16, -2) if algo == MFMA else (0, 16)):
+    for part in ((0, 16, -2, -3) if algo == MFMA else (0, 16)):
         got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, ctx, 0.3, 5, part, algo)
         np.testing.assert_array_equal(got[0], np.repeat(H.to_float(vl[0][0], dtype), 4, axis=0))
         assert (got[1] == 0).all()
@@ -255,7 +256,7 @@ def test_every_block_size(dtype, algo, bs):
     nb = sum((n + bs - 1) // bs for n in ctxs) + 5
     kc, vc, tab = H.paginate(kl, vl, bs, nb, rng, dtype)
     ref = pao.decode_concat(q, kc, vc, tab, np.array(ctxs), 1 / math.sqrt(d))
-    for part in (0, -1, max(bs, 256)):
+    for part in (0, -1, max(bs, 256)) + ((-3,) if algo == MFMA else ()):
         got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, np.array(ctxs), 1 / math.sqrt(d),
                            None, part, algo)
         H.assert_close_to_oracle(got, ref, dtype, f"bs {bs} partition {part}")
@@ -285,7 +286,7 @@ def test_group_sizes_mfma(G):
     vl = [S._normal(rng, (n, 2, 128), "bf16") for n in ctxs]
     kc, vc, tab = H.paginate(kl, vl, 16, 60, rng, "bf16")
     ref = pao.decode_concat(q, kc, vc, tab, np.array(ctxs), 0.09)
-    for part in (0, 128, -2):
+    for part in (0, 128, -2, -3):
         got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, np.array(ctxs), 0.09, None, part,
                            MFMA)
         H.assert_close_to_oracle(got, ref, "bf16", f"G {G} partition {part}")
@@ -332,7 +333,7 @@ def test_physical_placement_and_repeats_do_not_change_bits(dtype, algo):
     kl = [S._normal(rng, (n, 4, 128), dtype) for n in ctxs]
     vl = [S._normal(rng, (n, 4, 128), dtype) for n in ctxs]
     outs = []
-    parts = (0, 512, -2) if algo == MFMA else (0, 512)
+    parts = (0, 512, -2, -3) if algo == MFMA else (0, 512)
     for seed in (10, 11):
         kc, vc, tab = H.paginate(kl, vl, 16, 200, np.random.default_rng(seed), dtype)
         kd, vd = H.to_dev(kc), H.to_dev(vc)
@@ -345,7 +346,7 @@ def test_physical_placement_and_repeats_do_not_change_bits(dtype, algo):
         np.testing.assert_array_equal(a, b)
 
 
-@pytest.mark.parametrize("part", [512, -2])
+@pytest.mark.parametrize("part", [512, -2, -3])
 def test_phases_equal_one_call(part):
     w, kd, vd, kh, vh = full("long_split_bf16")
     ctx, tab, q = w.ctx_at(0), w.tables_at(0), w.q[0]
@@ -361,9 +362,11 @@ def test_phases_equal_one_call(part):
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
 
 
+@pytest.mark.parametrize("mode", [-2, -3])
 @pytest.mark.parametrize("ctxs,hkv,G", [([20000, 37], 1, 16), ([1, 2, 3, 40000], 2, 4),
-                                        ([16, 16, 16, 17], 3, 5), ([0, 5000, 0], 1, 8)])
-def test_balanced_split_cuts_anywhere(ctxs, hkv, G):
+                                        ([16, 16, 16, 17], 3, 5), ([0, 5000, 0], 1, 8),
+                                        ([0, 0, 0, 0, 0, 3], 2, 2), ([70000], 1, 4)])
+def test_balanced_split_cuts_anywhere(ctxs, hkv, G, mode):
     """The balanced split cuts contexts at arbitrary tiles, down to one tile
     per wavefront; the merged result matches the oracle."""
     rng = np.random.default_rng(sum(ctxs) + G)
@@ -375,9 +378,9 @@ def test_balanced_split_cuts_anywhere(ctxs, hkv, G):
     kc, vc, tab = H.paginate(kl, vl, bs, nb, rng, "bf16")
     ctx = np.array(ctxs, dtype=np.int32)
     ref = pao.decode_concat(q, kc, vc, tab, ctx, 1 / math.sqrt(d))
-    got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, ctx, 1 / math.sqrt(d), None,
-                       pa.PA_PARTITION_BALANCED, MFMA)
-    H.assert_close_to_oracle(got, ref, "bf16", f"balanced {ctxs}")
+    got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, ctx, 1 / math.sqrt(d), None, mode,
+                       MFMA)
+    H.assert_close_to_oracle(got, ref, "bf16", f"split mode {mode} {ctxs}")
 
 
 def test_copy_on_write_variant_of_shared_prefix():
@@ -433,8 +436,82 @@ def test_copy_on_write_variant_of_shared_prefix():
     ref = pao.decode_concat(q, kh, vh, tab, ctx, cfg.scale)
     got = H.gpu_decode(q, kd, vd, tab, ctx, cfg.scale, None, 512, MFMA)
     H.assert_close_to_oracle(got, ref, "bf16", "copy-on-write variant")
+    for mode in (pa.PA_PARTITION_SHARED, pa.PA_PARTITION_BALANCED, 0):
+        other = H.gpu_decode(q, kd, vd, tab, ctx, cfg.scale, None, mode, MFMA)
+        H.assert_close_to_oracle(other, ref, "bf16", f"copy-on-write variant, mode {mode}")
     kl = [np.concatenate(x) for x in logical_k]
     vl = [np.concatenate(x) for x in logical_v]
     kc2, vc2, tab2 = H.paginate(kl, vl, bs, B * cfg.max_blocks_per_seq, rng, "bf16")
     got2 = H.gpu_decode(q, H.to_dev(kc2), H.to_dev(vc2), tab2, ctx, cfg.scale, None, 512, MFMA)
     np.testing.assert_array_equal(got, got2)
+
+
+# --------------------------------------------------------------------------
+# shared-prefix read dedup
+# --------------------------------------------------------------------------
+def mixed_sharing_case(G, bs, seed):
+    """Thirteen sequences over a pool of random blocks: prompt families P
+    (10 blocks), Q (6) and R (4) referenced by several sequences at the same
+    logical positions (forks with and without private tails), a prefix-only
+    reference, two sequences that share a partly filled block with different
+    visible rows, an empty context, P's blocks at shifted positions, and an
+    unrelated long sequence.  Rows that no reference can see are NaN, so a
+    read that leaks into a result shows."""
+    rng = np.random.default_rng(seed)
+    hkv, d, nb = 2, 128, 400
+    kc = S._normal(rng, (nb, hkv, bs, d), "bf16")
+    vc = S._normal(rng, (nb, hkv, bs, d), "bf16")
+    ids = iter(int(x) for x in rng.permutation(nb))
+
+    def blocks(n):
+        return [next(ids) for _ in range(n)]
+
+    P, Q, R = blocks(10), blocks(6), blocks(4)
+    # (shared prefix, context length): private blocks complete each table
+    spec = [(P, 10 * bs + 40), (P, 10 * bs + 5), (P[:3], 2 * bs + 9), ([], 0), (R, 3 * bs + 12),
+            (R, 3 * bs + 9), (P, 10 * bs), (P[:5], 6 * bs + 4), (Q, 6 * bs + 1), (Q, 5 * bs + 10),
+            ([P[1], P[0], P[2]], 3 * bs), ([], 62 * bs + 8), (P, 12 * bs + 7)]
+    B = len(spec)
+    tab = np.full((B, 64), -1, dtype=np.int32)
+    visible = np.zeros(nb, dtype=np.int64)
+    for b, (prefix, n) in enumerate(spec):
+        need = (n + bs - 1) // bs
+        assert need >= len(prefix)
+        bl = prefix + blocks(need - len(prefix))
+        tab[b, :len(bl)] = bl
+        for j, x in enumerate(bl):
+            visible[x] = max(visible[x], min(bs, n - bs * j))
+    for x in range(nb):
+        kc[x, :, visible[x]:, :] = H.NAN_BITS["bf16"]
+        vc[x, :, visible[x]:, :] = H.NAN_BITS["bf16"]
+    ctx = np.array([n for _, n in spec], dtype=np.int32)
+    q = S._normal(rng, (B, hkv * G, d), "bf16")
+    return q, kc, vc, tab, ctx
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("G", [1, 3, 4, 5, 8, 16])
+def test_shared_mode_mixed_sharing(G, bs):
+    """Packs of 4, 2 or 1 sequences (by group size) read each distinct block
+    once; every sequence still gets its own plain decode result."""
+    q, kc, vc, tab, ctx = mixed_sharing_case(G, bs, seed=10 * G + bs)
+    ref = pao.decode_concat(q, kc, vc, tab, ctx, 0.08)
+    kd, vd = H.to_dev(kc), H.to_dev(vc)
+    for mode in (pa.PA_PARTITION_SHARED, pa.PA_PARTITION_BALANCED):
+        got = H.gpu_decode(q, kd, vd, tab, ctx, 0.08, None, mode, MFMA)
+        H.assert_close_to_oracle(got, ref, "bf16", f"G {G} bs {bs} mode {mode}")
+        assert (got[3] == 0).all()
+
+
+def test_shared_mode_full_size_all_rows():
+    """Every row of the forked workload in shared-prefix mode agrees with the
+    balanced split within the bf16 tolerance (sampled rows are pinned to the
+    oracle above), and repeated calls give the same bits."""
+    w, kd, vd, kh, vh = full("shared_prefix_bf16")
+    ctx, tab, q = w.ctx_at(0), w.tables_at(0), w.q[0]
+    a = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, None, pa.PA_PARTITION_SHARED, MFMA)
+    b = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, None, pa.PA_PARTITION_BALANCED, MFMA)
+    c = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, None, pa.PA_PARTITION_SHARED, MFMA)
+    assert np.isfinite(a).all()
+    assert H.row_rel_err(a, b).max() <= 1e-2
+    np.testing.assert_array_equal(a, c)
