@@ -36,6 +36,9 @@ namespace pa {
 #define PA_MFMA_DEPTH 1
 #endif
 // Occupancy hint: waves per SIMD the register allocation must allow (0: none).
+#ifndef PA_SPLIT_WAVES_PER_EU
+#define PA_SPLIT_WAVES_PER_EU 2
+#endif
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 3
 #endif
@@ -185,8 +188,8 @@ __device__ __forceinline__ int tiles_of_uniform(const DecodeParams &p, int b) {
 }
 
 __global__ __launch_bounds__(kWave)
-#if PA_MFMA_WAVES > 0
-__attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES)))
+#if PA_SPLIT_WAVES_PER_EU > 0
+__attribute__((amdgpu_waves_per_eu(PA_SPLIT_WAVES_PER_EU)))
 #endif
 void decode_mfma_balanced_kernel(const DecodeParams args, const int32_t *__restrict__ tables,
                                  const int32_t *__restrict__ ctx_lens, void *__restrict__ out,
@@ -209,6 +212,7 @@ void decode_mfma_balanced_kernel(const DecodeParams args, const int32_t *__restr
     const int w = xcd_remap(blockIdx.x, W);
     const int B = p.num_seqs;
     const int PT = p.partition_size / kTile;   // tiles per partition; 0: free cuts
+    extern __shared__ float park[];             // [ring_slots][group][kParkRow]
 
     // tile prefix over sequences: lane i owns sequences [i K, i K + K)
     const int K = (B + kWave - 1) / kWave;
@@ -263,19 +267,51 @@ void decode_mfma_balanced_kernel(const DecodeParams args, const int32_t *__restr
         Acc a;
         acc_init(a);
         if (PT > 0) {
+            // Each partition's state is parked in this wavefront's LDS and
+            // written out when the ring is full or the unit's range ends.
+            // A global store inside the tile loop would make the next
+            // tile's wait also wait for the store's completion (one
+            // counter covers loads and stores), stalling the stream once
+            // per partition; LDS writes are counted apart.
             const int n_parts = (Tb + PT - 1) / PT;
-            run_tiles(p, b, g, t_begin, t_end, n, qv, a, ln, PT, [&](int t) {
+            const int G = p.group;
+            int first = t_begin / PT;   // partition of ring slot 0
+            int held = 0;
+            auto flush = [&]() {
+                for (int k = 0; k < held; k++) {
+                    if (ln.row16 < G) {
+                        const float *src = park + (k * G + ln.row16) * kParkRow;
+                        const size_t prow =
+                            ((size_t)b * p.num_q_heads + g * G + ln.row16) * p.num_partitions +
+                            first + k;
+                        float *dst = p.ws_acc + prow * kD + 32 * ln.grp;
+#pragma unroll
+                        for (int i = 0; i < 8; i++)
+                            *(f32x4 *)(dst + 4 * i) = *(const f32x4 *)(src + 32 * ln.grp + 4 * i);
+                        if (ln.grp == 0) {
+                            p.ws_m[prow] = src[kD];
+                            p.ws_l[prow] = src[kD + 1];
+                        }
+                    }
+                }
+                first += held;
+                held = 0;
+            };
+            run_tiles(p, b, g, t_begin, t_end, n, qv, a, ln, PT, [&](int) {
                 acc_finish(a);
                 if (n_parts == 1) {
                     store_final(p, b, g, a, ln);
-                } else if (ln.row16 < p.group) {
-                    const size_t prow =
-                        ((size_t)b * p.num_q_heads + g * p.group + ln.row16) * p.num_partitions +
-                        t / PT;
-                    store_partial(p.ws_m + prow, p.ws_l + prow, p.ws_acc + prow * kD, a, ln);
+                } else {
+                    if (held == p.ring_slots) flush();
+                    if (ln.row16 < G) {
+                        float *dst = park + (held * G + ln.row16) * kParkRow;
+                        store_partial(dst + kD, dst + kD + 1, dst, a, ln);
+                    }
+                    held++;
                 }
                 acc_init(a);
             });
+            flush();
         } else {
             run_tiles(p, b, g, t_begin, t_end, n, qv, a, ln, 0, NoEmit{});
             acc_finish(a);
@@ -292,9 +328,14 @@ void decode_mfma_balanced_kernel(const DecodeParams args, const int32_t *__restr
 
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
     if (p.num_units == 0) return hipSuccess;
-    if (p.persistent)
-        hipLaunchKernelGGL(decode_mfma_balanced_kernel, dim3(p.num_units), dim3(kWave), 0, stream,
-                           p, p.block_tables, p.context_lens, p.out, p.ws_m, p.ws_l, p.ws_acc);
+    if (p.persistent) {
+        const size_t lds = p.partition_size > 0
+                               ? (size_t)p.ring_slots * p.group * kParkRow * sizeof(float)
+                               : 0;
+        hipLaunchKernelGGL(decode_mfma_balanced_kernel, dim3(p.num_units), dim3(kWave), lds,
+                           stream, p, p.block_tables, p.context_lens, p.out, p.ws_m, p.ws_l,
+                           p.ws_acc);
+    }
     else
         hipLaunchKernelGGL(decode_mfma_kernel, dim3(p.num_units), dim3(kWave), 0, stream, p);
     return hipGetLastError();

@@ -62,7 +62,9 @@ class Config:
     dtype: str                      # "f32" or "bf16"
     scale: float
     description: str
-    partition_size: int = -1        # -1: the library chooses
+    # split mode the benchmark launches: -1 the library chooses, -3 reads
+    # blocks shared inside a pack of sequences once, > 0 fixed partitions
+    partition_size: int = -1
     # context lengths: ("fixed", [..]) | ("uniform", lo, hi) | ("const", n)
     ctx_rule: tuple = ()
     # prefix sharing: None | ("random_group", n_members, n_shared_blocks, min_ctx)
@@ -93,7 +95,7 @@ CONFIGS = {
         name="shared_prefix_bf16", seed=4, num_seqs=256, num_q_heads=32, num_kv_heads=8,
         head_dim=128, block_size=16, num_blocks=16384, max_blocks_per_seq=160, dtype="bf16",
         scale=1 / math.sqrt(128), ctx_rule=("const", 2560), sharing=("fork", 32, 8, 2048),
-        partition_size=0,
+        partition_size=-3,
         description="bf16 shared-prefix parallel sampling: 32 prompts of 2048 tokens x 8 samples, "
                     "512 private tokens each (ctx 2560), 32 q / 8 kv heads, head_dim 128, block 16"),
     "long_split_bf16": Config(
@@ -174,11 +176,19 @@ class Workload:
         return int(self.ctx_at(step).astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * es
 
     def kv_unique_bytes(self, step: int = 0) -> int:
+        """K and V bytes of the distinct token rows the decode step can see:
+        a physical block referenced by several sequences counts once, with
+        the most rows any of them sees (rows past a context are not read)."""
         c = self.cfg
         es = 2 if c.dtype == "bf16" else 4
         t = self.tables_at(step)
-        ids = np.unique(t[t >= 0])
-        return int(ids.size) * c.block_size * c.num_kv_heads * c.head_dim * 2 * es
+        ctx = self.ctx_at(step).astype(np.int64)
+        j = np.arange(t.shape[1], dtype=np.int64)[None, :]
+        vis = np.clip(ctx[:, None] - j * c.block_size, 0, c.block_size)
+        use = vis > 0
+        best = np.zeros(c.num_blocks, dtype=np.int64)
+        np.maximum.at(best, t[use], vis[use])
+        return int(best.sum()) * c.num_kv_heads * c.head_dim * 2 * es
 
 
 def _context_lengths(cfg: Config, rng) -> np.ndarray:
