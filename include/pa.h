@@ -117,9 +117,11 @@ int pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_ca
  * Partition mode the library uses when pa_decode / pa_decode_partitions get
  * partition_size == PA_PARTITION_AUTO for these sizes and PA_ALGO_AUTO:
  * 0 (single pass, no workspace), PA_PARTITION_BALANCED, or a multiple of
- * block_size.  A pure function of its arguments (with PA_ALGO_VECTOR a
- * balanced choice becomes 512-token partitions, or single pass when the
- * context fits one).
+ * block_size.  A pure function of its arguments.  Where the vector kernel
+ * runs (every shape the matrix-core kernels do not take, or PA_ALGO_VECTOR)
+ * the partition is the power of two from 64 to 512 tokens (at least
+ * block_size) that gives about 8192 wavefronts for contexts of
+ * max_context_len, or single pass for small problems.
  */
 int pa_decode_auto_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_context_len, int dtype);
@@ -162,9 +164,9 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
  *                 wavefronts take equal contiguous shares; pieces of a
  *                 context cut between wavefronts are merged by log-sum-exp;
  *                 PA_PARTITION_SHARED: like PA_PARTITION_BALANCED, but
- *                 consecutive sequences are taken in packs (4 when the
- *                 group size is at most 4, 2 up to 8, else 1) whose query
- *                 heads share one wavefront, and a physical block that
+ *                 consecutive sequences are taken in packs (8 when the
+ *                 group size is at most 4, 4 up to 8, 2 up to 16) whose
+ *                 query heads share one wavefront, and a physical block that
  *                 several members of a pack reference at the same logical
  *                 position (a shared prefix, e.g. forked samples) is read
  *                 once for all of them; a planning kernel counts the

@@ -41,9 +41,13 @@ constexpr int kBalancedWaves = PA_BALANCED_WAVES;
 constexpr int kSharedWaves = PA_SHARED_WAVES;
 constexpr size_t kParkBytes = 36 * 1024;
 
-// Sequences per pack in shared-prefix mode: as many as fit the 16 columns,
-// at most 4.
-int pack_of(int group) { return group <= 4 ? 4 : (group <= 8 ? 2 : 1); }
+// Sequences per pack in shared-prefix mode: the largest power of two, at
+// most 8, whose query heads fit the 32 columns of a wavefront.
+int pack_of(int group) {
+    int k = 8;
+    while (k > 1 && k * group > pa::kMaxCols) k >>= 1;
+    return k;
+}
 
 bool is_split_mode(int partition) {
     return partition == PA_PARTITION_BALANCED || partition == PA_PARTITION_SHARED;
@@ -55,6 +59,23 @@ bool balanced_applies(int dtype, int head_dim, int block_size, int num_q_heads,
            num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads <= 16;
 }
 
+// Partition size for the vector kernel (one wavefront per (sequence, KV
+// head, partition)): small enough that about kVectorWaves wavefronts have
+// work when every context is max_context_len long -- the kernel hides
+// memory latency by occupancy -- but at least 64 tokens, at most 512, a
+// power of two and a multiple of block_size.  Small problems run in one
+// pass (the merge would cost more than it saves).
+constexpr int64_t kVectorWaves = 8192;
+
+int vector_partition(int num_seqs, int num_kv_heads, int block_size, int max_context_len) {
+    const int64_t work = (int64_t)max_context_len * num_seqs * num_kv_heads;
+    if (work <= 64 * 1024) return 0;
+    int p = 64;
+    while (p < 512 && (int64_t)p * kVectorWaves < work) p <<= 1;
+    if (p < block_size) p = block_size;
+    return max_context_len > p ? p : 0;
+}
+
 // Resolve the partition size: 0 = single pass, PA_PARTITION_BALANCED, or a
 // multiple of block_size.
 int resolve_partition(int partition_size, int num_seqs, int num_q_heads, int num_kv_heads,
@@ -63,7 +84,7 @@ int resolve_partition(int partition_size, int num_seqs, int num_q_heads, int num
     const int p = pa_decode_auto_partition(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                            block_size, max_context_len, dtype);
     if (p == PA_PARTITION_BALANCED && algo == PA_ALGO_VECTOR)
-        return max_context_len > 512 && 512 % block_size == 0 ? 512 : 0;
+        return vector_partition(num_seqs, num_kv_heads, block_size, max_context_len);
     return p;
 }
 
@@ -78,16 +99,16 @@ WorkspaceLayout layout(int num_seqs, int num_q_heads, int head_dim, int max_cont
                        int partition, int group = 1) {
     WorkspaceLayout w{};
     if (partition == PA_PARTITION_SHARED) {
-        // cost [P] | pos [P][max_tiles + 1] | dir [W][2] | m, l [W][2][16] |
-        // acc [W][2][16][head_dim]
-        const size_t slots = (size_t)kSharedWaves * 2 * pa::kMaxGroup;
+        // cost [P] | items [P][pack * max_tiles][4] | dir [W][2] | m, l [W][2][32] |
+        // acc [W][2][32][head_dim]
+        const size_t slots = (size_t)kSharedWaves * 2 * pa::kMaxCols;
         w.pack = pack_of(group);
         w.num_packs = (num_seqs + w.pack - 1) / w.pack;
         w.max_tiles = (max_context_len + 15) / 16;
         w.cost_off = 0;
         w.pos_off = round256((size_t)w.num_packs * sizeof(int32_t));
-        w.dir_off = w.pos_off +
-                    round256((size_t)w.num_packs * (w.max_tiles + 1) * sizeof(int32_t));
+        w.dir_off = w.pos_off + round256((size_t)w.num_packs * w.pack * w.max_tiles * 4 *
+                                         sizeof(int32_t));
         w.m_off = w.dir_off + round256((size_t)kSharedWaves * 2 * sizeof(int32_t));
         w.l_off = w.m_off + round256(slots * sizeof(float));
         w.acc_off = w.l_off + round256(slots * sizeof(float));
@@ -219,7 +240,7 @@ pa::SharedParams shared_params(const DecodeArgs &a, const WorkspaceLayout &w, ch
     p.max_tiles = w.max_tiles;
     p.num_waves = kSharedWaves;
     p.ws_cost = (int *)(ws + w.cost_off);
-    p.ws_pos = (int *)(ws + w.pos_off);
+    p.ws_items = (int *)(ws + w.pos_off);
     p.ws_dir = (int *)(ws + w.dir_off);
     p.ws_m = (float *)(ws + w.m_off);
     p.ws_l = (float *)(ws + w.l_off);
@@ -264,12 +285,10 @@ int pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_ca
 
 int pa_decode_auto_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_context_len, int dtype) {
-    (void)num_seqs;
     if (!block_size_ok(block_size)) return 0;
     if (balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads))
         return PA_PARTITION_BALANCED;
-    const int partition = block_size > 512 ? block_size : 512;
-    return max_context_len > partition ? partition : 0;
+    return vector_partition(num_seqs, num_kv_heads, block_size, max_context_len);
 }
 
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

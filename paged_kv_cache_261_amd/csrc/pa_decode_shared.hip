@@ -6,96 +6,70 @@
 // reference counts of KVBlock; "CS349E 第 7 讲 01_paged_attention.py",
 // demo 3: n samples share the prompt's blocks).  Decode then reads the same
 // shared block once per sample.  Here NPK consecutive sequences form a pack
-// whose G query heads each fill NPK*G of the 16 matrix-core columns of one
-// wavefront, so for every tile index t the wavefront loads each distinct
-// physical block among the pack's block-table entries once and folds it into
-// the columns of the sequences that reference it (pa_mfma_tile.h).  The
+// whose query heads fill NPK*G of the 32 columns of one wavefront (two
+// 16-column matrix-core groups that share every K/V load; NPK is the largest
+// power of two up to 8 that fits), and each distinct physical block among
+// the pack's block-table entries at a tile index is loaded once and folded
+// into the columns of the sequences that reference it (pa_mfma_tile.h).  The
 // result per sequence is the plain decode result: sharing changes no value
 // (demo 3 observations).
 //
 // Three kernels:
-//  1. plan_shared_kernel, one wavefront per pack: the cost of tile index t is
-//     the number of distinct block ids among the members that reach it;
-//     pos_k[t] = sum of costs before t, U_k = pos_k[T_k].
+//  1. plan_shared_kernel, one wavefront per pack: lists the pack's items.
+//     At tile index t, member i owns an item when it is the first member (in
+//     order) that reaches t with its block id; the item is (block id, t, the
+//     members with that id, the most rows any of them sees).  Items are
+//     stored in tile-index order; U_k = the pack's item count.
 //  2. decode_shared_kernel: W persistent wavefronts split the stream of
-//     costs (KV head slowest, then pack, then tile index) into equal shares;
-//     a wavefront computes every tile index whose position lies in its
-//     share.  A pack it covers whole is finished in place; otherwise its
-//     state goes to one of the wavefront's two partial slots (only its first
-//     and last pack can be partial) and the slot is recorded in a small
-//     directory.
+//     items (KV head slowest, then pack, then item) into equal shares; each
+//     item is one tile load and one update of the columns of its members, so
+//     a share may start or end anywhere.  A pack a wavefront covers whole is
+//     finished in place; otherwise its state goes to one of the wavefront's
+//     two partial slots (only its first and last pack can be partial) and
+//     the slot is recorded in a small directory.
 //  3. reduce_shared_kernel: per (KV head, pack, column), merge the recorded
 //     pieces by log-sum-exp.
 #include "pa_mfma_tile.h"
 
 namespace pa {
 
-namespace {
-
-__device__ __forceinline__ int shared_tiles_of(const SharedParams &p, int b) {
-    if (b >= p.num_seqs) return 0;
-    return (clamp_ctx(p.context_lens[b], p.max_context_len) + kTile - 1) / kTile;
-}
-
-// Index of the first entry >= v in the non-decreasing pos[0..n] (pos[n] >= v),
-// found by the whole wavefront: each round probes 64 evenly spaced entries of
-// the candidate range [lo, hi] (the last probe at hi) and keeps the stretch
-// between the last probe below v and the first one at or above it.
-__device__ __forceinline__ int wave_lower_bound(const int *pos, int n, int v) {
-    const int lane = threadIdx.x;
-    int lo = 0, hi = n;                                // answer in [lo, hi]
-    while (hi - lo >= kWave) {
-        const int step = (hi - lo + kWave - 2) / (kWave - 1);   // 63 step >= hi - lo
-        const int idx = min(lo + lane * step, hi);
-        const unsigned long long ge = __ballot(pos[idx] >= v);  // lane 63 probes hi
-        const int f = __builtin_ctzll(ge);
-        if (f == 0) return lo;
-        const int nlo = lo + (f - 1) * step + 1;
-        hi = min(lo + f * step, hi);
-        lo = nlo;
-    }
-    const unsigned long long ge = __ballot(pos[min(lo + lane, hi)] >= v);
-    return lo + __builtin_ctzll(ge);
-}
-
-}  // namespace
-
 // ---------------------------------------------------------------------------
-// 1. Plan: distinct tiles per tile index of each pack.
+// 1. Plan: the item list of each pack.
 // ---------------------------------------------------------------------------
+// Item record (16 bytes): block id (0 when out of range, with rows 0), tile
+// index, rows | member mask << 8, unused.
 template <int NPK>
 __global__ __launch_bounds__(kWave) void plan_shared_kernel(const SharedParams p) {
     const int k = blockIdx.x;
     const int lane = threadIdx.x;
-    int T[NPK];
+    int n[NPK];
     int maxT = 0;
 #pragma unroll
     for (int i = 0; i < NPK; i++) {
-        T[i] = shared_tiles_of(p, k * NPK + i);
-        maxT = max(maxT, T[i]);
+        const int b = k * NPK + i;
+        n[i] = b < p.num_seqs ? clamp_ctx(p.context_lens[b], p.max_context_len) : 0;
+        maxT = max(maxT, (n[i] + kTile - 1) / kTile);
     }
-    int *pos = p.ws_pos + (size_t)k * (p.max_tiles + 1);
+    int4 *items = (int4 *)p.ws_items + (size_t)k * NPK * p.max_tiles;
     int running = 0;
     for (int t0 = 0; t0 < maxT; t0 += kWave) {
         const int t = t0 + lane;
+        int id[NPK];
+        bool v[NPK];
+#pragma unroll
+        for (int i = 0; i < NPK; i++) {
+            v[i] = t * kTile < n[i];
+            id[i] = v[i] ? p.block_tables[(size_t)(k * NPK + i) * p.max_blocks_per_seq +
+                                          ((t * kTile) >> p.log2_block)]
+                         : -1;
+        }
         int cost = 0;
-        if (t < maxT) {
-            int id[NPK];
-            bool v[NPK];
 #pragma unroll
-            for (int i = 0; i < NPK; i++) {
-                v[i] = t < T[i];
-                id[i] = v[i] ? p.block_tables[(size_t)(k * NPK + i) * p.max_blocks_per_seq +
-                                              ((t * kTile) >> p.log2_block)]
-                             : -1;
-            }
+        for (int i = 0; i < NPK; i++) {
+            bool dup = false;
 #pragma unroll
-            for (int i = 0; i < NPK; i++) {
-                bool dup = false;
-#pragma unroll
-                for (int j = 0; j < i; j++) dup |= v[j] && id[j] == id[i];
-                cost += (v[i] && !dup) ? 1 : 0;
-            }
+            for (int j = 0; j < i; j++) dup |= v[j] && id[j] == id[i];
+            cost += (v[i] && !dup) ? 1 : 0;
         }
         int incl = cost;
 #pragma unroll
@@ -103,13 +77,29 @@ __global__ __launch_bounds__(kWave) void plan_shared_kernel(const SharedParams p
             const int y = __shfl_up(incl, off);
             if (lane >= off) incl += y;
         }
-        if (t < maxT) pos[t + 1] = running + incl;
+        // this tile index's items go to [running + incl - cost, running + incl)
+        int q = running + incl - cost;
+#pragma unroll
+        for (int i = 0; i < NPK; i++) {
+            bool dup = false;
+#pragma unroll
+            for (int j = 0; j < i; j++) dup |= v[j] && id[j] == id[i];
+            if (v[i] && !dup) {
+                int mask = 0, maxn = 0;
+#pragma unroll
+                for (int m = 0; m < NPK; m++)
+                    if (v[m] && id[m] == id[i]) {
+                        mask |= 1 << m;
+                        maxn = max(maxn, n[m]);
+                    }
+                const bool ok = (unsigned)id[i] < (unsigned)p.num_blocks;
+                const int rows = ok ? min(kTile, maxn - t * kTile) : 0;
+                items[q++] = make_int4(ok ? id[i] : 0, t, rows | (mask << 8), 0);
+            }
+        }
         running += __shfl(incl, kWave - 1);
     }
-    if (lane == 0) {
-        pos[0] = 0;
-        p.ws_cost[k] = running;
-    }
+    if (lane == 0) p.ws_cost[k] = running;
 }
 
 // ---------------------------------------------------------------------------
@@ -119,81 +109,16 @@ __global__ __launch_bounds__(kWave) void plan_shared_kernel(const SharedParams p
 #define PA_SHARED_WAVES_PER_EU 2
 #endif
 
-// Per-tile-index view of the pack: block id, reach and visible rows of each
-// member, all uniform (scalar).
-template <int NPK>
-struct PackTile {
-    int id[NPK];
-    bool valid[NPK];
-    int nvis[NPK];
-};
-
-template <int NPK>
-__device__ __forceinline__ void pack_tile_read(const SharedParams &p, const int32_t *const (&tab)[NPK],
-                                               const int (&T)[NPK], const int (&n)[NPK], int t,
-                                               PackTile<NPK> &pt) {
-#pragma unroll
-    for (int i = 0; i < NPK; i++) {
-        pt.valid[i] = t < T[i];
-        pt.id[i] = pt.valid[i] ? tab[i][(t * kTile) >> p.log2_block] : -1;
-        pt.nvis[i] = min(kTile, n[i] - t * kTile);
-    }
-}
-
-// Items of tile index t of a pack: member i owns an item when it is the first
-// member (in order) that reaches t with its block id; the item loads that
-// tile once for the members with the same id (mask), reading the most rows
-// any of them can see (rows).  owners: bit i set when member i owns an item,
-// so popcount(owners) is the plan's cost of t.  A block id outside the pool
-// gives rows == 0: nothing is loaded or computed for it.
-struct PackItem {
-    int rows;
-    int mask;
-    int t;
-    size_t tile_byte_off;
-};
-
-template <int NPK>
-__device__ __forceinline__ void pack_items(const SharedParams &p, const PackTile<NPK> &pt, int t,
-                                           int g, PackItem (&items)[NPK], int &owners) {
-    const int bs_mask = (1 << p.log2_block) - 1;
-    owners = 0;
-#pragma unroll
-    for (int i = 0; i < NPK; i++) {
-        bool dup = false;
-        int mask = 0, rows = 0;
-#pragma unroll
-        for (int m = 0; m < NPK; m++) {
-            const bool same = pt.valid[i] && pt.valid[m] && pt.id[m] == pt.id[i];
-            if (m < i) dup |= same;
-            if (m >= i && same) {
-                mask |= 1 << m;
-                rows = max(rows, pt.nvis[m]);
-            }
-        }
-        const bool own = pt.valid[i] && !dup;
-        const bool ok = own && (unsigned)pt.id[i] < (unsigned)p.num_blocks;
-        owners |= own ? 1 << i : 0;
-        items[i].rows = ok ? rows : 0;
-        items[i].mask = mask;
-        items[i].t = t;
-        items[i].tile_byte_off =
-            ((((size_t)(ok ? pt.id[i] : 0) * p.num_kv_heads + g) << p.log2_block) +
-             ((t * kTile) & bs_mask)) * (size_t)kRowBytes;
-    }
-}
-
-template <int NPK>
+template <int NPK, int NCG>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PA_SHARED_WAVES_PER_EU)))
-void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ tables,
-                          const int32_t *__restrict__ ctx_lens, void *__restrict__ out,
-                          float *__restrict__ ws_m, float *__restrict__ ws_l,
-                          float *__restrict__ ws_acc, int *__restrict__ ws_dir,
-                          const int *__restrict__ ws_cost, const int *__restrict__ ws_pos) {
-    // restrict arguments: the stores cannot alias the tables, so the
-    // per-tile block-id reads stay on the scalar unit
+void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ ctx_lens,
+                          void *__restrict__ out, float *__restrict__ ws_m,
+                          float *__restrict__ ws_l, float *__restrict__ ws_acc,
+                          int *__restrict__ ws_dir, const int *__restrict__ ws_cost,
+                          const int4 *__restrict__ ws_items) {
+    // restrict arguments: the stores cannot alias the item lists, so the
+    // per-item reads stay on the scalar unit
     SharedParams p = args;
-    p.block_tables = tables;
     p.context_lens = ctx_lens;
     p.out = out;
     const int lane = threadIdx.x;
@@ -207,7 +132,7 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ t
         ws_dir[2 * w + 1] = -1;
     }
 
-    // cost prefix over packs: lane i owns packs [i K, i K + K)
+    // item-count prefix over packs: lane i owns packs [i K, i K + K)
     const int K = (NPACK + kWave - 1) / kWave;
     int local = 0;
     for (int j = 0; j < K; j++) {
@@ -225,17 +150,28 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ t
     const int total = TT * p.num_kv_heads;
     const int C = (total + W - 1) / W;
 
-    // this lane's column: member im of the pack, head j of the group
-    const int im = ln.row16 / G;
-    const int hj = ln.row16 - im * G;
-    const bool col_real = im < NPK;
+    // this lane's columns, one per column group of 16: column
+    // cg * 16 + row16 is head hj of member im of the pack
+    int im[NCG], hj[NCG];
+    bool col_real[NCG];
+#pragma unroll
+    for (int cg = 0; cg < NCG; cg++) {
+        const int col = cg * 16 + ln.row16;
+        im[cg] = col / G;
+        hj[cg] = col - im[cg] * G;
+        col_real[cg] = im[cg] < NPK;
+    }
 
+    const char *kbase = (const char *)p.k_cache;
+    const char *vbase = (const char *)p.v_cache;
+    const int bs_mask = (1 << p.log2_block) - 1;
     const int x1 = min(w * C + C, total);
     int x = w * C;
     int slot = 0;
     while (x < x1) {
         const int g = x / TT;
         const int r = x - g * TT;
+        // the pack holding stream position r: find its lane, then walk
         const unsigned long long own = __ballot(r >= excl && r < incl);
         const int jl = __builtin_ctzll(own);
         int base = __builtin_amdgcn_readfirstlane(__shfl(excl, jl));
@@ -246,130 +182,83 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ t
             k++;
             Uk = __builtin_amdgcn_readfirstlane(ws_cost[k]);
         }
-        const int off = r - base;
-        const int lim = min(Uk, off + (x1 - x));
-        x += lim - off;
+        const int q_begin = r - base;                  // items [q_begin, q_end) of pack k
+        const int q_end = min(Uk, q_begin + (x1 - x));
+        x += q_end - q_begin;
 
-        int T[NPK], n[NPK];
-        const int32_t *tab[NPK];
-        int maxT = 0;
+        // this lane's columns within the pack
+        int b_col[NCG], n_col[NCG];
+        bool col_ok[NCG];
+        bf16x8 qv[NCG][4];
+        Acc a[NCG];
 #pragma unroll
-        for (int i = 0; i < NPK; i++) {
-            const int b = k * NPK + i;
-            n[i] = b < p.num_seqs
-                       ? __builtin_amdgcn_readfirstlane(
-                             clamp_ctx(p.context_lens[b], p.max_context_len))
-                       : 0;
-            T[i] = (n[i] + kTile - 1) / kTile;
-            maxT = max(maxT, T[i]);
-            tab[i] = p.block_tables + (size_t)min(b, p.num_seqs - 1) * p.max_blocks_per_seq;
-        }
-        const int *pos = ws_pos + (size_t)k * (p.max_tiles + 1);
-        const int t_begin = __builtin_amdgcn_readfirstlane(wave_lower_bound(pos, maxT, off));
-        const int t_end = __builtin_amdgcn_readfirstlane(wave_lower_bound(pos, maxT, lim));
-        if (t_begin >= t_end) continue;
-
-        // this lane's column within the pack
-        const int b_col = k * NPK + (col_real ? im : 0);
-        const bool col_ok = col_real && b_col < p.num_seqs;
-        int n_col = 0;
-#pragma unroll
-        for (int i = 0; i < NPK; i++)
-            if (i == im) n_col = n[i];
-        bf16x8 qv[4];
-        {
+        for (int cg = 0; cg < NCG; cg++) {
+            b_col[cg] = k * NPK + (col_real[cg] ? im[cg] : 0);
+            col_ok[cg] = col_real[cg] && b_col[cg] < p.num_seqs;
+            n_col[cg] = col_ok[cg] ? clamp_ctx(p.context_lens[b_col[cg]], p.max_context_len) : 0;
             const char *qrow = (const char *)p.q +
-                               (((size_t)(col_ok ? b_col : 0) * p.num_q_heads + g * G +
-                                 (col_ok ? hj : 0)) * kD + 8 * ln.grp) * 2;
+                               (((size_t)(col_ok[cg] ? b_col[cg] : 0) * p.num_q_heads + g * G +
+                                 (col_ok[cg] ? hj[cg] : 0)) * kD + 8 * ln.grp) * 2;
 #pragma unroll
             for (int kk = 0; kk < 4; kk++) {
                 u32x4 raw = *(const u32x4 *)(qrow + 64 * kk);
-                if (!col_ok) raw = (u32x4){0u, 0u, 0u, 0u};
-                qv[kk] = __builtin_bit_cast(bf16x8, raw);
+                if (!col_ok[cg]) raw = (u32x4){0u, 0u, 0u, 0u};
+                qv[cg][kk] = __builtin_bit_cast(bf16x8, raw);
             }
+            acc_init(a[cg]);
         }
-        Acc a;
-        acc_init(a);
 
-        // the items of tile indices t_begin..t_end-1 in order, owners in
-        // member order within a tile index; the loads of the next item are
-        // issued before the current one is computed.  A tile index's items
-        // are worked out when the loop enters it, from the view read one
-        // tile index ahead, and only then is the next view requested, so
-        // waiting for a view never waits for the newest reads.
-        const char *kbase = (const char *)p.k_cache;
-        const char *vbase = (const char *)p.v_cache;
-        const int nitems = __builtin_amdgcn_readfirstlane(pos[t_end] - pos[t_begin]);
-        PackTile<NPK> view;
-        // the owners' items of the current tile index, in member order, as a
-        // queue that only ever moves by whole positions (every index below is
-        // a constant, so the queue stays in scalar registers)
-        PackItem queue[NPK];
-        int left = 0;
-        int t_cur = t_begin - 1;
-        pack_tile_read(p, tab, T, n, t_begin, view);
-        auto take = [&]() {
-            if (left == 0) {   // enter the next tile index (each has an owner)
-                t_cur++;
-                PackItem items[NPK];
-                int owners;
-                pack_items(p, view, t_cur, g, items, owners);
-                pack_tile_read(p, tab, T, n, min(t_cur + 1, t_end - 1), view);
-#pragma unroll
-                for (int m = NPK - 1; m >= 0; m--)
-                    if ((owners >> m) & 1) {
-#pragma unroll
-                        for (int k = NPK - 1; k > 0; k--) queue[k] = queue[k - 1];
-                        queue[0] = items[m];
-                    }
-                left = __builtin_popcount(owners);
-            }
-            PackItem r = queue[0];
-#pragma unroll
-            for (int k = 0; k + 1 < NPK; k++) queue[k] = queue[k + 1];
-            left--;
-            // uniform by construction; say so, or a buffer descriptor built
-            // from it would be made lane by lane
-            r.rows = __builtin_amdgcn_readfirstlane(r.rows);
-            r.mask = __builtin_amdgcn_readfirstlane(r.mask);
-            r.t = __builtin_amdgcn_readfirstlane(r.t);
-            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)r.tile_byte_off);
-            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(r.tile_byte_off >> 32));
-            r.tile_byte_off = ((size_t)hi << 32) | lo;
-            return r;
+        // items q_begin .. q_end-1; the loads of item q+1 are issued before
+        // item q is computed, and the record of item q+2 is read meanwhile
+        const int4 *list = ws_items + (size_t)k * NPK * p.max_tiles;
+        auto issue = [&](const int4 &it, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+            const size_t off = ((((size_t)it.x * p.num_kv_heads + g) << p.log2_block) +
+                                ((it.y * kTile) & bs_mask)) * (size_t)kRowBytes;
+            load_tile_rows(kbase, vbase, off, it.z & 0xff, ln, kr, vr);
         };
         u32x4 kr[2][4], vr[2][4];
-        PackItem itm[2];
-        itm[0] = take();
-        load_tile_rows(kbase, vbase, itm[0].tile_byte_off, itm[0].rows, ln, kr[0], vr[0]);
-        for (int q0 = 0; q0 < nitems; q0 += 2) {
+        int4 rec[2];
+        rec[0] = list[q_begin];
+        int4 ahead = list[min(q_begin + 1, q_end - 1)];
+        issue(rec[0], kr[0], vr[0]);
+        for (int q0 = q_begin; q0 < q_end; q0 += 2) {
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 const int q = q0 + j;
-                if (q >= nitems) break;
-                PackItem next{0, 0, t_cur, 0};
-                if (q + 1 < nitems) next = take();
-                itm[(j + 1) & 1] = next;
-                load_tile_rows(kbase, vbase, next.tile_byte_off, next.rows, ln,
-                               kr[(j + 1) & 1], vr[(j + 1) & 1]);
+                if (q >= q_end) break;
+                const int4 nxt = q + 1 < q_end ? ahead : make_int4(0, 0, 0, 0);
+                ahead = list[min(q + 2, q_end - 1)];
+                rec[(j + 1) & 1] = nxt;
+                issue(nxt, kr[(j + 1) & 1], vr[(j + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the wait
-                const PackItem &it = itm[j];
-                if (it.rows > 0) {
-                    const bool in_mask = col_ok && ((it.mask >> im) & 1);
-                    const int nv = in_mask ? n_col - it.t * kTile : 0;
-                    tile_update<true>(kr[j], vr[j], qv, nv, p.scale_log2, a, ln);
+                const int4 it = rec[j];
+                if ((it.z & 0xff) > 0) {
+                    const int mask = it.z >> 8;
+#pragma unroll
+                    for (int cg = 0; cg < NCG; cg++) {
+                        const bool in_mask = col_ok[cg] && ((mask >> im[cg]) & 1);
+                        const int nv = in_mask ? n_col[cg] - it.y * kTile : 0;
+                        tile_update<true>(kr[j], vr[j], qv[cg], nv, p.scale_log2, a[cg], ln);
+                    }
                 }
             }
         }
-        acc_finish(a);
-        if (t_begin == 0 && t_end == maxT) {
-            if (col_ok)
-                store_row((char *)out +
-                              ((size_t)b_col * p.num_q_heads + g * G + hj) * kD * 2,
-                          a, ln);
-        } else {
-            const size_t prow = ((size_t)w * 2 + slot) * kMaxGroup + ln.row16;
-            store_partial(ws_m + prow, ws_l + prow, ws_acc + prow * kD, a, ln);
+
+        const bool whole = q_begin == 0 && q_end == Uk;
+#pragma unroll
+        for (int cg = 0; cg < NCG; cg++) {
+            acc_finish(a[cg]);
+            if (whole) {
+                if (col_ok[cg])
+                    store_row((char *)out + ((size_t)b_col[cg] * p.num_q_heads + g * G + hj[cg]) *
+                                                kD * 2,
+                              a[cg], ln);
+            } else {
+                const size_t prow = ((size_t)w * 2 + slot) * kMaxCols + cg * 16 + ln.row16;
+                store_partial(ws_m + prow, ws_l + prow, ws_acc + prow * kD, a[cg], ln);
+            }
+        }
+        if (!whole) {
             if (lane == 0) ws_dir[2 * w + slot] = g * NPACK + k;
             slot = 1;
         }
@@ -379,96 +268,140 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ t
 // ---------------------------------------------------------------------------
 // 3. Merge.
 // ---------------------------------------------------------------------------
-template <typename V>
-__device__ __forceinline__ V block128_sum(V x, V *red) {
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = x;
-    __syncthreads();
-    x = red[0] + red[1];
-    __syncthreads();
-    return x;
-}
+// One workgroup of 4 wavefronts per (KV head, pack) unit.  The unit's
+// pieces -- the partial slots whose directory entry names it, among the
+// wavefronts whose shares overlap the unit -- are listed once in LDS in
+// ascending order; then all 32 columns are merged at once, 8 threads per
+// column and 16 dims per thread, pieces summed in list order.
+constexpr int kReduceThreads = 256;
 
-template <int NPK>
-__global__ __launch_bounds__(kD) void reduce_shared_kernel(const SharedParams p,
-                                                           const int *__restrict__ ws_dir,
-                                                           const int *__restrict__ ws_cost) {
-    __shared__ int red[2];
-    const int c = blockIdx.x % kMaxGroup;
-    const int unit = blockIdx.x / kMaxGroup;       // g * NPACK + k
+template <int NPK, int NCG>
+__global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
+    const SharedParams p, const int *__restrict__ ws_dir, const int *__restrict__ ws_cost) {
+    extern __shared__ int lds[];                   // red[4] | count | pieces[2 W]
+    int *red = lds, *count = lds + 4, *pieces = lds + 8;
+    const int unit = blockIdx.x;                   // g * NPACK + k
     const int NPACK = p.num_packs;
     const int k = unit % NPACK, g = unit / NPACK;
     const int G = p.group;
-    const int im = c / G;
-    if (im >= NPK) return;
-    const int b = k * NPK + im;
-    if (b >= p.num_seqs) return;
-    const int i = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+
+    // position of the unit in the item stream (as the decode kernel split it)
     int before = 0, all = 0;
-    for (int kk = i; kk < NPACK; kk += kD) {
+    for (int kk = tid; kk < NPACK; kk += kReduceThreads) {
         const int u = ws_cost[kk];
         all += u;
         if (kk < k) before += u;
     }
-    const int S = block128_sum(before, red);
-    const int TT = block128_sum(all, red);
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+        before += __shfl_xor(before, o);
+        all += __shfl_xor(all, o);
+    }
+    if (lane == 0) {
+        red[wave] = before;
+        pieces[wave] = all;   // scratch until the list is built
+    }
+    __syncthreads();
+    const int S = red[0] + red[1] + red[2] + red[3];
+    const int TT = pieces[0] + pieces[1] + pieces[2] + pieces[3];
     const int U = ws_cost[k];
-    uint16_t *o = (uint16_t *)p.out + ((size_t)b * p.num_q_heads + (size_t)g * G + (c - im * G)) * kD;
-    if (U == 0) {
-        o[i] = 0;
+    __syncthreads();
+    int first = 0, last = -1;
+    if (U > 0) {
+        const int C = (TT * p.num_kv_heads + p.num_waves - 1) / p.num_waves;
+        const int start = g * TT + S;
+        first = start / C;
+        last = (start + U - 1) / C;
+    }
+    if (wave == 0) {
+        int n = 0;
+        for (int e0 = 2 * first; e0 < 2 * last + 2; e0 += kWave) {
+            const int e = e0 + lane;
+            const bool hit = e < 2 * last + 2 && ws_dir[e] == unit;
+            const unsigned long long m = __ballot(hit);
+            if (hit) pieces[n + __builtin_popcountll(m & ((1ull << lane) - 1))] = e;
+            n += __builtin_popcountll(m);
+        }
+        if (lane == 0) *count = n;
+    }
+    __syncthreads();
+    const int npieces = *count;
+
+    // 8 lanes per column, 16 dims per lane: the 32 columns at once
+    const int c = tid / 8, sub = tid % 8;
+    const int im = c / G;
+    const int b = k * NPK + im;
+    if (c >= NCG * 16 || im >= NPK || b >= p.num_seqs) return;
+    uint16_t *o = (uint16_t *)p.out +
+                  ((size_t)b * p.num_q_heads + (size_t)g * G + (c - im * G)) * kD + 16 * sub;
+    if (U == 0) {                                   // empty context
+        *(uint4 *)o = make_uint4(0u, 0u, 0u, 0u);
+        *(uint4 *)(o + 8) = make_uint4(0u, 0u, 0u, 0u);
         return;
     }
-    const int C = (TT * p.num_kv_heads + p.num_waves - 1) / p.num_waves;
-    const int start = g * TT + S;
-    const int first = start / C, last = (start + U - 1) / C;
+    if (npieces == 0) return;                       // finished by one wavefront
     float M = -INFINITY;
-    int pieces = 0;
-    for (int w = first; w <= last; w++)
-        for (int s = 0; s < 2; s++)
-            if (ws_dir[2 * w + s] == unit) {
-                M = fmaxf(M, p.ws_m[((size_t)w * 2 + s) * kMaxGroup + c]);
-                pieces++;
-            }
-    if (pieces == 0) return;                       // finished by one wavefront
-    float num = 0.f, den = 0.f;
+    for (int q = 0; q < npieces; q++) M = fmaxf(M, p.ws_m[(size_t)pieces[q] * kMaxCols + c]);
+    float num[16], den = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e++) num[e] = 0.f;
     if (M != -INFINITY) {
-        for (int w = first; w <= last; w++)
-            for (int s = 0; s < 2; s++)
-                if (ws_dir[2 * w + s] == unit) {
-                    const size_t prow = ((size_t)w * 2 + s) * kMaxGroup + c;
-                    const float mq = p.ws_m[prow];
-                    if (mq == -INFINITY) continue;
-                    const float wq = __builtin_amdgcn_exp2f(mq - M);
-                    den = fmaf(wq, p.ws_l[prow], den);
-                    num = fmaf(wq, p.ws_acc[prow * kD + i], num);
-                }
+        for (int q = 0; q < npieces; q++) {
+            const size_t prow = (size_t)pieces[q] * kMaxCols + c;
+            const float mq = p.ws_m[prow];
+            const float wq = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - M);
+            den = fmaf(wq, p.ws_l[prow], den);
+            const float4 *src = (const float4 *)(p.ws_acc + prow * kD + 16 * sub);
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const float4 a4 = src[v];
+                num[4 * v + 0] = fmaf(wq, a4.x, num[4 * v + 0]);
+                num[4 * v + 1] = fmaf(wq, a4.y, num[4 * v + 1]);
+                num[4 * v + 2] = fmaf(wq, a4.z, num[4 * v + 2]);
+                num[4 * v + 3] = fmaf(wq, a4.w, num[4 * v + 3]);
+            }
+        }
     }
-    o[i] = f32_to_bf16(den > 0.f ? num / den : 0.f);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    uint32_t wv[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        wv[e] = (uint32_t)f32_to_bf16(num[2 * e] * inv) |
+                ((uint32_t)f32_to_bf16(num[2 * e + 1] * inv) << 16);
+    *(uint4 *)o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    *(uint4 *)(o + 8) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
 }
 
 // ---------------------------------------------------------------------------
-template <int NPK>
+template <int NPK, int NCG>
 static hipError_t launch_shared_t(const SharedParams &p, int phase, hipStream_t stream) {
     if (phase & 1) {
         hipLaunchKernelGGL(plan_shared_kernel<NPK>, dim3(p.num_packs), dim3(kWave), 0, stream, p);
-        hipLaunchKernelGGL(decode_shared_kernel<NPK>, dim3(p.num_waves), dim3(kWave), 0, stream, p,
-                           p.block_tables, p.context_lens, p.out, p.ws_m, p.ws_l, p.ws_acc,
-                           p.ws_dir, p.ws_cost, p.ws_pos);
+        hipLaunchKernelGGL((decode_shared_kernel<NPK, NCG>), dim3(p.num_waves), dim3(kWave), 0,
+                           stream, p, p.context_lens, p.out, p.ws_m, p.ws_l, p.ws_acc, p.ws_dir,
+                           p.ws_cost, (const int4 *)p.ws_items);
     }
     if (phase & 2)
-        hipLaunchKernelGGL(reduce_shared_kernel<NPK>,
-                           dim3((unsigned)p.num_kv_heads * p.num_packs * kMaxGroup), dim3(kD), 0,
-                           stream, p, p.ws_dir, p.ws_cost);
+        hipLaunchKernelGGL((reduce_shared_kernel<NPK, NCG>),
+                           dim3((unsigned)p.num_kv_heads * p.num_packs), dim3(kReduceThreads),
+                           (8 + 2 * (size_t)p.num_waves) * sizeof(int), stream, p, p.ws_dir,
+                           p.ws_cost);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_shared(const SharedParams &p, int phase, hipStream_t stream) {
     if (p.num_seqs == 0) return hipSuccess;
+    // columns used: pack * group <= 32, in one or two groups of 16
+    const bool two = p.pack * p.group > 16;
     switch (p.pack) {
-    case 4: return launch_shared_t<4>(p, phase, stream);
-    case 2: return launch_shared_t<2>(p, phase, stream);
-    default: return launch_shared_t<1>(p, phase, stream);
+    case 8: return two ? launch_shared_t<8, 2>(p, phase, stream)
+                       : launch_shared_t<8, 1>(p, phase, stream);
+    case 4: return two ? launch_shared_t<4, 2>(p, phase, stream)
+                       : launch_shared_t<4, 1>(p, phase, stream);
+    case 2: return two ? launch_shared_t<2, 2>(p, phase, stream)
+                       : launch_shared_t<2, 1>(p, phase, stream);
+    default: return launch_shared_t<1, 1>(p, phase, stream);
     }
 }
 

@@ -84,15 +84,18 @@ struct SharedParams {
     float scale_log2;
     int pack;                 // sequences per pack
     int num_packs;            // ceil(num_seqs / pack)
-    int max_tiles;            // ceil(max_context_len / 16); pos rows hold max_tiles + 1
+    int max_tiles;            // ceil(max_context_len / 16)
     int num_waves;            // persistent wavefronts
-    int *ws_cost;             // [num_packs] distinct tiles per pack
-    int *ws_pos;              // [num_packs][max_tiles + 1] cost before each tile index
+    int *ws_cost;             // [num_packs] items (distinct tiles) per pack
+    int *ws_items;            // [num_packs][pack * max_tiles] item records, 4 ints each
     int *ws_dir;              // [W][2] pack unit held by each partial slot, or -1
-    float *ws_m;              // [W][2][16]
-    float *ws_l;              // [W][2][16]
-    float *ws_acc;            // [W][2][16][128]
+    float *ws_m;              // [W][2][32]
+    float *ws_l;              // [W][2][32]
+    float *ws_acc;            // [W][2][32][128]
 };
+
+// Query-head columns of one shared-prefix wavefront: two groups of 16.
+constexpr int kMaxCols = 32;
 
 // Work-unit numbering shared by the decode kernels.  Workgroups are handed
 // to the 8 XCDs round-robin (workgroup w runs on XCD w % 8); this remaps the
