@@ -39,7 +39,6 @@ constexpr int kBalancedWaves = PA_BALANCED_WAVES;
 #define PA_SHARED_WAVES 1024
 #endif
 constexpr int kSharedWaves = PA_SHARED_WAVES;
-constexpr size_t kParkBytes = 36 * 1024;
 
 // Sequences per pack in shared-prefix mode: the largest power of two, at
 // most 8, whose query heads fit the 32 columns of a wavefront.
@@ -210,9 +209,7 @@ int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *
     p.scale_log2 = a.scale * 1.4426950408889634f;
     p.num_units = (int)units;
     p.persistent = persistent ? 1 : 0;
-    // partition states parked in LDS per wavefront: up to 36 KiB, so the
-    // four wavefronts of a compute unit (one per SIMD) fit its LDS
-    p.ring_slots = (int)(kParkBytes / ((size_t)p.group * pa::kParkRow * sizeof(float)));
+
     const hipError_t e = use_mfma ? pa::launch_decode_mfma(p, stream)
                                   : pa::launch_decode_vector(p, a.head_dim, a.dtype, stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

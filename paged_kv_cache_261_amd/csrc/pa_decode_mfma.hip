@@ -33,14 +33,14 @@ namespace pa {
 
 // Prefetch depth: tiles whose loads are in flight while a tile is computed.
 #ifndef PA_MFMA_DEPTH
-#define PA_MFMA_DEPTH 1
+#define PA_MFMA_DEPTH 3
 #endif
 // Occupancy hint: waves per SIMD the register allocation must allow (0: none).
 #ifndef PA_SPLIT_WAVES_PER_EU
-#define PA_SPLIT_WAVES_PER_EU 2
+#define PA_SPLIT_WAVES_PER_EU 1
 #endif
 #ifndef PA_MFMA_WAVES
-#define PA_MFMA_WAVES 3
+#define PA_MFMA_WAVES 2
 #endif
 
 constexpr int kDepth = PA_MFMA_DEPTH;
@@ -212,7 +212,6 @@ void decode_mfma_balanced_kernel(const DecodeParams args, const int32_t *__restr
     const int w = xcd_remap(blockIdx.x, W);
     const int B = p.num_seqs;
     const int PT = p.partition_size / kTile;   // tiles per partition; 0: free cuts
-    extern __shared__ float park[];             // [ring_slots][group][kParkRow]
 
     // tile prefix over sequences: lane i owns sequences [i K, i K + K)
     const int K = (B + kWave - 1) / kWave;
@@ -267,51 +266,38 @@ void decode_mfma_balanced_kernel(const DecodeParams args, const int32_t *__restr
         Acc a;
         acc_init(a);
         if (PT > 0) {
-            // Each partition's state is parked in this wavefront's LDS and
-            // written out when the ring is full or the unit's range ends.
-            // A global store inside the tile loop would make the next
-            // tile's wait also wait for the store's completion (one
-            // counter covers loads and stores), stalling the stream once
-            // per partition; LDS writes are counted apart.
+            // Each partition's softmax state (m, l, acc over its own tokens)
+            // is merged into the run's state by the log-sum-exp rule as soon
+            // as the partition ends; the run -- this wavefront's consecutive
+            // partitions of the unit -- then leaves one merged state, in the
+            // row of its first partition, and marks its other partitions
+            // empty (m = -inf, l = 0) for the merge kernel.  Writing every
+            // partition's accumulator instead would put a burst of stores at
+            // the end of the run, which costs more than the whole merge.
             const int n_parts = (Tb + PT - 1) / PT;
             const int G = p.group;
-            int first = t_begin / PT;   // partition of ring slot 0
-            int held = 0;
-            auto flush = [&]() {
-                for (int k = 0; k < held; k++) {
-                    if (ln.row16 < G) {
-                        const float *src = park + (k * G + ln.row16) * kParkRow;
-                        const size_t prow =
-                            ((size_t)b * p.num_q_heads + g * G + ln.row16) * p.num_partitions +
-                            first + k;
-                        float *dst = p.ws_acc + prow * kD + 32 * ln.grp;
-#pragma unroll
-                        for (int i = 0; i < 8; i++)
-                            *(f32x4 *)(dst + 4 * i) = *(const f32x4 *)(src + 32 * ln.grp + 4 * i);
-                        if (ln.grp == 0) {
-                            p.ws_m[prow] = src[kD];
-                            p.ws_l[prow] = src[kD + 1];
-                        }
-                    }
-                }
-                first += held;
-                held = 0;
-            };
+            Acc run;
+            acc_init(run);
             run_tiles(p, b, g, t_begin, t_end, n, qv, a, ln, PT, [&](int) {
                 acc_finish(a);
-                if (n_parts == 1) {
-                    store_final(p, b, g, a, ln);
-                } else {
-                    if (held == p.ring_slots) flush();
-                    if (ln.row16 < G) {
-                        float *dst = park + (held * G + ln.row16) * kParkRow;
-                        store_partial(dst + kD, dst + kD + 1, dst, a, ln);
-                    }
-                    held++;
-                }
+                acc_merge(run, a);
                 acc_init(a);
             });
-            flush();
+            if (n_parts == 1) {
+                store_final(p, b, g, run, ln);
+            } else if (ln.row16 < G) {
+                const size_t prow =
+                    ((size_t)b * p.num_q_heads + g * G + ln.row16) * p.num_partitions +
+                    t_begin / PT;
+                store_partial(p.ws_m + prow, p.ws_l + prow, p.ws_acc + prow * kD, run, ln);
+                if (ln.grp == 0) {
+                    const int k_end = (t_end + PT - 1) / PT - t_begin / PT;
+                    for (int k = 1; k < k_end; k++) {
+                        p.ws_m[prow + k] = -INFINITY;
+                        p.ws_l[prow + k] = 0.f;
+                    }
+                }
+            }
         } else {
             run_tiles(p, b, g, t_begin, t_end, n, qv, a, ln, 0, NoEmit{});
             acc_finish(a);
@@ -328,14 +314,9 @@ void decode_mfma_balanced_kernel(const DecodeParams args, const int32_t *__restr
 
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
     if (p.num_units == 0) return hipSuccess;
-    if (p.persistent) {
-        const size_t lds = p.partition_size > 0
-                               ? (size_t)p.ring_slots * p.group * kParkRow * sizeof(float)
-                               : 0;
-        hipLaunchKernelGGL(decode_mfma_balanced_kernel, dim3(p.num_units), dim3(kWave), lds,
-                           stream, p, p.block_tables, p.context_lens, p.out, p.ws_m, p.ws_l,
-                           p.ws_acc);
-    }
+    if (p.persistent)
+        hipLaunchKernelGGL(decode_mfma_balanced_kernel, dim3(p.num_units), dim3(kWave), 0, stream,
+                           p, p.block_tables, p.context_lens, p.out, p.ws_m, p.ws_l, p.ws_acc);
     else
         hipLaunchKernelGGL(decode_mfma_kernel, dim3(p.num_units), dim3(kWave), 0, stream, p);
     return hipGetLastError();

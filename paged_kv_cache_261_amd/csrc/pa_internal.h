@@ -40,12 +40,7 @@ struct DecodeParams {
     int num_units;            // wavefronts: NP * Hkv * B (grid), or W (persistent)
     int persistent;           // matrix-core path: num_units persistent wavefronts share
                               // the tile stream; partition_size 0 = free cuts
-    int ring_slots;           // persistent fixed partitions: partition states a
-                              // wavefront parks in LDS before writing them out
 };
-
-// LDS row of one parked column: head_dim accumulators, m, l, padding to 16 B.
-constexpr int kParkRow = 132;
 
 struct ReduceParams {
     void *out;

@@ -103,6 +103,19 @@ __device__ __forceinline__ void acc_init(Acc &a) {
 // Sum the lane shares of l over the 4 lane groups (after the last tile).
 __device__ __forceinline__ void acc_finish(Acc &a) { a.lsum = xor32_sum(xor16_sum(a.lsum)); }
 
+// dst <- the log-sum-exp merge of two finished states (each lane holds its
+// column's full l): M = max(m1, m2), weights 2^(m - M), an empty state
+// (m = -inf) weighing 0.
+__device__ __forceinline__ void acc_merge(Acc &dst, const Acc &src) {
+    const float M = fmaxf(dst.m, src.m);
+    const float wd = dst.m == -INFINITY ? 0.f : fast_exp2(dst.m - M);
+    const float ws = src.m == -INFINITY ? 0.f : fast_exp2(src.m - M);
+#pragma unroll
+    for (int nn = 0; nn < 8; nn++) dst.o[nn] = dst.o[nn] * wd + src.o[nn] * ws;
+    dst.lsum = dst.lsum * wd + src.lsum * ws;
+    dst.m = M;
+}
+
 // Fold one tile into the state.  kr / vr: the tile's K and V operands as
 // loaded; nv: rows of the tile visible to this lane's column (tokens at or
 // past nv are selected out).  With kMaybeEmpty a column may see no visible

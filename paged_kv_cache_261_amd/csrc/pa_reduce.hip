@@ -8,7 +8,9 @@
 // exactly (up to rounding):
 //     M = max_q m_q,  w_q = 2^(m_q - M),  out = sum_q w_q acc_q / sum_q w_q l_q.
 // Pieces are summed in ascending order: no atomics, deterministic.  A piece
-// with nothing visible has m_q = -inf and weight 0.
+// with nothing visible has m_q = -inf and weight 0, and its accumulator is
+// not read (the matrix-core split leaves the accumulators of the partitions
+// it merged in-wave unwritten).
 //
 // One workgroup per (sequence, query head) row, one thread per element of
 // head_dim.  The piece weights are computed once, by the threads in turn,
@@ -85,9 +87,12 @@ __device__ __forceinline__ void merge_row(T *out, int n, const float *m, const f
     if (D <= kWave) __syncthreads();
     float num = 0.f;
     if (M != -INFINITY) {
+        // a piece of weight 0 is skipped, not multiplied: an empty piece's
+        // accumulator is never written
         const float *a = acc + i;
 #pragma unroll 8
-        for (int q = 0; q < n; q++) num = fmaf(weights[q], a[(size_t)q * as], num);
+        for (int q = 0; q < n; q++)
+            if (weights[q] != 0.f) num = fmaf(weights[q], a[(size_t)q * as], num);
     }
     store_out(out + i, den > 0.f ? num / den : 0.f);
 }
