@@ -74,6 +74,17 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
+def decode_kernel_name(c, part, algo):
+    """The kernel the decode phase runs (the roofline's dominant kernel)."""
+    mfma = (c.dtype == "bf16" and c.head_dim == 128 and c.block_size >= 16
+            and c.num_q_heads // c.num_kv_heads <= 16 and algo != "vector")
+    if part == -3:
+        return "decode_shared_kernel (after plan_shared_kernel)"
+    if not mfma:
+        return "decode_vector_kernel"
+    return "decode_mfma_kernel" if part == 0 else "decode_mfma_balanced_kernel"
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -108,26 +119,38 @@ def cpu_baseline(w, target_seconds):
     ctx, tab, q = w.ctx_at(0), w.tables_at(0), w.q[0]
     es = 2 if c.dtype == "bf16" else 4
 
-    def run(n):
+    def run(n, threads):
         t = time.perf_counter()
         pao.slot_write(kh, vh, w.step_k[0][:n], w.step_v[0][:n], w.step_slots[0][:n],
                        c.block_size)
-        pao.decode_concat(q[:n], kh, vh, tab[:n], ctx[:n], c.scale, nthreads=cores)
+        pao.decode_concat(q[:n], kh, vh, tab[:n], ctx[:n], c.scale, nthreads=threads)
         return time.perf_counter() - t
 
+    def kv_bytes(n):
+        return int(ctx[:n].astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * es
+
+    # all cores: grow the prefix until one run takes a quarter of the budget
+    # (or the batch is whole), then repeat it within the budget; median
     n = min(c.num_seqs, max(1, cores))
-    dt = run(n)
+    dt = run(n, cores)
     while n < c.num_seqs and dt < target_seconds / 4:
         n = min(c.num_seqs, n * 2)
-        dt = run(n)
-    if n < c.num_seqs and dt < target_seconds:
-        n = min(c.num_seqs, max(n, int(n * target_seconds / max(dt, 1e-3))))
-        dt = run(n)
-    kv = int(ctx[:n].astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * es
-    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        dt = run(n, cores)
+    times = [dt]
+    while sum(times) < target_seconds and len(times) < 40:
+        times.append(run(n, cores))
+    dt = statistics.median(times)
+    # one core, on a prefix about 1/cores as long
+    n1 = max(1, n // cores)
+    t1 = run(n1, 1)
+    return {"value": round(kv_bytes(n) / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
             "sample": f"first {n} of {c.num_seqs} sequences of {c.name} "
-                      f"(sum ctx {int(ctx[:n].sum())}), one step, {dt:.2f} s",
-            "tokens_per_s": round(n / dt, 3)}
+                      f"(sum ctx {int(ctx[:n].sum())}), one step, median of {len(times)} "
+                      f"runs, {dt:.3f} s each",
+            "tokens_per_s": round(n / dt, 3),
+            "single_thread": {"value": round(kv_bytes(n1) / t1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"first {n1} sequences, {t1:.3f} s"}}
 
 
 def main():
@@ -241,6 +264,28 @@ def main():
     achieved = decode_alg / (main_ms * 1e-3) / 1e9
     algo_name = args.algo
     traffic = load_traffic(args.config, algo_name, part)
+    kernel_name = decode_kernel_name(c, part, args.algo)
+
+    # (3) the decode phase with caches cold: a 1 GiB write between launches
+    # evicts L2 and the MALL (not timed)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(min(args.steps, 20)):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if part == 0:
+            pa.pa_decode(out, q, k_cache, v_cache, tables, ctx, c.scale, max_ctx, 0, None, algo,
+                         stream=stream)
+        else:
+            pa.pa_decode_partitions(out, q, k_cache, v_cache, tables, ctx, c.scale, max_ctx, part,
+                                    ws, algo, stream=stream)
+        e1.record(stream)
+        if part != 0:
+            pa.pa_decode_reduce(out, ctx, c.num_kv_heads, max_ctx, part, ws, stream=stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
 
     result = {
         "metric": METRIC,
@@ -266,13 +311,14 @@ def main():
                        "decode": round(main_ms, 5),
                        "reduce": round(statistics.mean(t_reduce), 5),
                        "step_events": round(statistics.mean(t_step), 5),
+                       "decode_cold_l2": round(statistics.median(cold), 5),
                        "decode_p10": round(float(np.percentile(t_main, 10)), 5),
                        "decode_p90": round(float(np.percentile(t_main, 90)), 5)},
         "bytes": {"kv_logical": kv_logical, "kv_unique": kv_unique,
                   "decode_algorithmic": decode_alg},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode (per-partition kernel)"},
+                     "traffic": traffic, "kernel": kernel_name},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
