@@ -253,6 +253,36 @@ def main():
     t_reduce = [e[2].elapsed_time(e[3]) for e in evs]
     t_step = [e[0].elapsed_time(e[3]) for e in evs]
 
+    # (4) copy-on-write block copies (pa_copy_blocks): up to 4096 pairs, each
+    # from a block the tables use into one they do not (the decode inputs
+    # stay intact)
+    used = np.unique(w.tables_at(0)[w.tables_at(0) >= 0])
+    free_blocks = np.setdiff1d(np.arange(c.num_blocks), used)
+    rng = np.random.default_rng(1234)
+    n_cp = int(min(4096, len(free_blocks)))
+    copy_rec = None
+    if n_cp > 0:
+        pairs = np.stack([rng.choice(used, size=n_cp), rng.permutation(free_blocks)[:n_cp]],
+                         axis=1).astype(np.int32)
+        pairs_d = dev_t(pairs)
+        for _ in range(3):
+            pa.pa_copy_blocks(k_cache, v_cache, pairs_d, stream=stream)
+        cp_ms = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pa.pa_copy_blocks(k_cache, v_cache, pairs_d, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cp_ms.append(e0.elapsed_time(e1))
+        block_bytes = c.num_kv_heads * c.block_size * c.head_dim * (2 if c.dtype == "bf16" else 4)
+        cp_bytes = 4 * n_cp * block_bytes                 # read + write, K and V
+        cp_t = statistics.median(cp_ms)
+        copy_rec = {"pairs": n_cp, "ms": round(cp_t, 5), "bytes": cp_bytes,
+                    "GBs": round(cp_bytes / (cp_t * 1e-3) / 1e9, 1),
+                    "frac": round(cp_bytes / (cp_t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "kernel": "copy_blocks_kernel"}
+
     es = 2 if c.dtype == "bf16" else 4
     kv_logical = w.kv_logical_bytes(0)
     kv_unique = w.kv_unique_bytes(0)
@@ -266,12 +296,13 @@ def main():
     traffic = load_traffic(args.config, algo_name, part)
     kernel_name = decode_kernel_name(c, part, args.algo)
 
-    # (3) the decode phase with caches cold: a 1 GiB write between launches
-    # evicts L2 and the MALL (not timed)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # (3) the decode phase with caches cold: reading a 1 GiB buffer between
+    # launches evicts L2 and the MALL (not timed; a read leaves no dirty
+    # lines to write back during the decode)
+    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)
     cold = []
     for _ in range(min(args.steps, 20)):
-        flush.fill_(1)
+        flush.sum()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         if part == 0:
@@ -319,6 +350,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kernel_name},
+        "copy_blocks": copy_rec,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

@@ -114,6 +114,28 @@ int pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_ca
                          void *stream);
 
 /*
+ * Copy-on-write block copies ("PagedAttention实现", cow_write: a block shared
+ * by several sequences is copied whole into a fresh block before one of them
+ * writes into it; "CS349E 第 7 讲 01_paged_attention.py", demo 3).  For every
+ * pair i with (src, dst) = (block_pairs[2 i], block_pairs[2 i + 1]):
+ *     k_cache[dst][:][:][:] = k_cache[src][:][:][:]   (all heads, all slots)
+ * and the same for V, bit-exact.  A pair with an id outside [0, num_blocks)
+ * or with src == dst is skipped.
+ *
+ *   k_cache,
+ *   v_cache      [num_blocks][num_kv_heads][block_size][head_dim] (in/out)
+ *   block_pairs  [num_pairs][2] int32, device memory               (in)
+ *
+ * The destinations must be distinct and none may be the source of another
+ * pair in the same call (the pairs are copied concurrently); a fresh block
+ * from the allocator always satisfies this.  Supported shapes and dtypes as
+ * for pa_reshape_and_cache.  num_pairs == 0 is a no-op.
+ */
+int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int num_pairs,
+                   int num_blocks, int num_kv_heads, int block_size, int head_dim, int dtype,
+                   void *stream);
+
+/*
  * Partition mode the library uses when pa_decode / pa_decode_partitions get
  * partition_size == PA_PARTITION_AUTO for these sizes and PA_ALGO_AUTO:
  * 0 (single pass, no workspace), PA_PARTITION_BALANCED, or a multiple of

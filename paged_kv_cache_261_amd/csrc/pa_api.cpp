@@ -280,6 +280,23 @@ int pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_ca
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int num_pairs,
+                   int num_blocks, int num_kv_heads, int block_size, int head_dim, int dtype,
+                   void *stream) {
+    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || !block_size_ok(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+    const int64_t block_bytes =
+        (int64_t)num_kv_heads * block_size * head_dim * (dtype == PA_BF16 ? 2 : 4);
+    if (block_bytes % 16) return PA_ERR_UNSUPPORTED;
+    const hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs,
+                                                num_blocks, block_bytes, (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 int pa_decode_auto_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_context_len, int dtype) {
     if (!block_size_ok(block_size)) return 0;

@@ -133,6 +133,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // Launchers: validate nothing (pa_api.cpp does), enqueue, return hipError_t.
+hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int num_pairs,
+                              int num_blocks, int64_t block_bytes, hipStream_t stream);
 hipError_t launch_cache_write(const void *k, const void *v, void *k_cache, void *v_cache,
                               const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
                               int head_dim, int num_blocks, int log2_block, int elem_bytes,

@@ -36,6 +36,7 @@ def _load():
     P, I, F, SZ = C.c_void_p, C.c_int, C.c_float, C.c_size_t
     sig = {
         "pa_reshape_and_cache": (I, [P, P, P, P, P, I, I, I, I, I, I, P]),
+        "pa_copy_blocks": (I, [P, P, P, I, I, I, I, I, I, P]),
         "pa_decode_auto_partition": (I, [I, I, I, I, I, I, I]),
         "pa_decode_workspace_size": (SZ, [I, I, I, I, I, I, I, I]),
         "pa_decode": (I, [P] * 6 + [I] * 8 + [F, I, P, SZ, I, I, P]),
@@ -99,6 +100,23 @@ def pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, stream=None):
                                     _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"),
                                     t, hkv, d, nb, bs, dt, _stream(k, stream)),
            "pa_reshape_and_cache")
+
+
+def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+    """Copy whole blocks src -> dst in both pools, for every row (src, dst) of
+    block_pairs ([n, 2] int32, on the GPU): the device side of copy-on-write."""
+    nb, hkv, bs, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must have the same shape and dtype")
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int32 [num_pairs, 2]")
+    n = block_pairs.shape[0]
+    if n == 0:
+        return
+    _check(lib.pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                              _dev(block_pairs, "block_pairs"), n, nb, hkv, bs, d,
+                              dtype_code(k_cache), _stream(k_cache, stream)),
+           "pa_copy_blocks")
 
 
 def pa_decode_auto_partition(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,

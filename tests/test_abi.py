@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"pa_reshape_and_cache", "pa_decode", "pa_decode_partitions",
                           "pa_decode_reduce", "pa_decode_workspace_size",
-                          "pa_decode_auto_partition", "pa_status_string"}
+                          "pa_decode_auto_partition", "pa_status_string", "pa_copy_blocks"}
     raw = C.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), n
@@ -144,3 +144,20 @@ def test_reduce_rejects_bad_arguments(lib):
     assert lib.pa_decode_reduce(A, A, 2, 8, 2, 128, 1000, -2, A, 4096, 1, Z) == WS
     assert lib.pa_decode_reduce(Z, A, 2, 8, 2, 128, 1000, 512, A, 1 << 20, 1, Z) == NULL
     assert lib.pa_decode_reduce(A, A, 0, 8, 2, 128, 1000, 512, Z, 0, 1, Z) == OK
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("args,status", [
+    ((A, A, A, -1, 64, 8, 16, 128, 1, Z), SHAPE),
+    ((A, A, A, 4, 0, 8, 16, 128, 1, Z), SHAPE),
+    ((A, A, A, 4, 64, 0, 16, 128, 1, Z), SHAPE),
+    ((A, A, A, 4, 64, 8, 12, 128, 1, Z), UNSUP),
+    ((A, A, A, 4, 64, 8, 16, 48, 1, Z), UNSUP),
+    ((A, A, A, 4, 64, 8, 16, 128, 3, Z), UNSUP),
+    ((Z, A, A, 4, 64, 8, 16, 128, 1, Z), NULL),
+    ((A, A, Z, 4, 64, 8, 16, 128, 1, Z), NULL),
+    ((A, MIS, A, 4, 64, 8, 16, 128, 1, Z), ALIGN),
+    ((Z, Z, Z, 0, 64, 8, 16, 128, 1, Z), OK),
+])
+def test_copy_blocks_rejects_bad_arguments(lib, args, status):
+    assert lib.pa_copy_blocks(*args) == status

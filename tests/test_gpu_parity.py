@@ -387,8 +387,9 @@ def test_copy_on_write_variant_of_shared_prefix():
     """Shared-prefix sampling with 2056-token prompts: the last prompt block
     holds 8 of 16 tokens, so the first private token of 7 of the 8 samples
     copies it ("PagedAttention实现" cow_write; lecture 7 demo 3: n - 1 copies).
-    The pool copy is mirrored on the device; the outputs must equal the
-    unshared layout bit for bit and match the oracle."""
+    The pool copy is made on the device by pa_copy_blocks; the pools must
+    stay bit-identical, the outputs must equal the unshared layout bit for bit
+    and match the oracle."""
     n_prompts, n_samples, prompt, private = 4, 8, 2056, 40
     hq, hkv, d, bs = 32, 8, 128, 16
     B = n_prompts * n_samples
@@ -420,8 +421,7 @@ def test_copy_on_write_variant_of_shared_prefix():
             if src >= 0:
                 copies += 1
                 pao.copy_block(kh, vh, src, dst)
-                kd[dst].copy_(kd[src])
-                vd[dst].copy_(vd[src])
+                pa.pa_copy_blocks(kd, vd, H.to_dev(np.array([[src, dst]], dtype=np.int32)))
             tk = S._normal(rng, (1, hkv, d), "bf16")
             tv = S._normal(rng, (1, hkv, d), "bf16")
             pao.slot_write(kh, vh, tk, tv, np.array([slot]), bs)
@@ -515,3 +515,93 @@ def test_shared_mode_full_size_all_rows():
     assert np.isfinite(a).all()
     assert H.row_rel_err(a, b).max() <= 1e-2
     np.testing.assert_array_equal(a, c)
+
+
+# --------------------------------------------------------------------------
+# copy-on-write block copies
+# --------------------------------------------------------------------------
+def copy_case(rng, nb, n_pairs, n_bad=0):
+    """n_pairs (src, dst) with distinct destinations that are no pair's source,
+    plus n_bad pairs the kernel must skip (ids out of range, src == dst)."""
+    perm = rng.permutation(nb)
+    dst = perm[:n_pairs]
+    src = rng.choice(perm[n_pairs:], size=n_pairs, replace=True)
+    pairs = np.stack([src, dst], axis=1).astype(np.int32)
+    bad = []
+    for i in range(n_bad):
+        bad.append([[-1, int(dst[0])], [int(src[0]), nb], [nb + 5, -7],
+                    [int(perm[-1]), int(perm[-1])]][i % 4])
+    if bad:
+        pairs = np.concatenate([pairs, np.array(bad, dtype=np.int32)])
+        pairs = pairs[rng.permutation(len(pairs))]
+    return pairs
+
+
+@pytest.mark.parametrize("dtype,hkv,bs,d,nb,n_pairs", [
+    ("bf16", 8, 16, 128, 4096, 224), ("f32", 8, 16, 64, 1024, 500), ("bf16", 1, 1, 16, 64, 30),
+    ("f32", 3, 256, 256, 40, 9), ("bf16", 2, 4, 32, 2048, 1000), ("f32", 1, 1, 16, 140000, 70000),
+])
+def test_copy_blocks_bit_exact(dtype, hkv, bs, d, nb, n_pairs):
+    """Device block copies equal the oracle's copy_block applied pair by pair,
+    every byte of both pools; invalid pairs change nothing."""
+    rng = np.random.default_rng(nb + n_pairs)
+    cfg = S.Config(name="cp", seed=0, num_seqs=1, num_q_heads=hkv, num_kv_heads=hkv,
+                   head_dim=d, block_size=bs, num_blocks=nb, max_blocks_per_seq=1, dtype=dtype,
+                   scale=1.0, description="")
+    kh = S._normal(rng, (nb, hkv, bs, d), dtype)
+    vh = S._normal(rng, (nb, hkv, bs, d), dtype)
+    kd, vd = H.to_dev(kh), H.to_dev(vh)
+    pairs = copy_case(rng, nb, n_pairs, n_bad=4)
+    note(f"[gpu parity] copy_blocks {dtype} Hkv {hkv} bs {bs} d {d} pairs {len(pairs)}")
+    pa.pa_copy_blocks(kd, vd, H.to_dev(pairs))
+    for s_, d_ in pairs:
+        if 0 <= s_ < nb and 0 <= d_ < nb and s_ != d_:
+            pao.copy_block(kh, vh, int(s_), int(d_))
+    np.testing.assert_array_equal(H.to_host(kd), kh)
+    np.testing.assert_array_equal(H.to_host(vd), vh)
+    del cfg
+
+
+def test_copy_blocks_then_decode_matches_oracle():
+    """Forks of one prompt, each appending into the half-full shared last
+    block: the allocator's copy-on-write pairs go to pa_copy_blocks in one
+    batch per step; decode over the result matches the oracle."""
+    rng = np.random.default_rng(77)
+    hq, hkv, d, bs, nb = 16, 4, 128, 16, 512
+    pool = Pool(nb, bs, free_order=rng.permutation(nb).astype(np.int32))
+    cfg = S.Config(name="cow2", seed=0, num_seqs=6, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                   block_size=bs, num_blocks=nb, max_blocks_per_seq=16, dtype="bf16", scale=0.1,
+                   description="")
+    kh, vh = H.empty_pool(cfg)
+    kd, vd = H.dev_empty_pool(cfg)
+    lead = pool.seq_new()
+    pk = S._normal(rng, (100, hkv, d), "bf16")
+    pv = S._normal(rng, (100, hkv, d), "bf16")
+    slots = np.array([pool.append(lead)[0] for _ in range(100)])
+    pao.slot_write(kh, vh, pk, pv, slots, bs)
+    H.dev_write(kd, vd, pk, pv, slots)
+    seqs = [lead] + [pool.fork(lead) for _ in range(5)]
+    for step in range(20):
+        pairs, step_slots = [], []
+        for s in seqs:
+            slot, src, dst = pool.append(s)
+            step_slots.append(slot)
+            if src >= 0:
+                pairs.append((src, dst))
+                pao.copy_block(kh, vh, src, dst)
+        if pairs:
+            pa.pa_copy_blocks(kd, vd, H.to_dev(np.array(pairs, dtype=np.int32)))
+        tk = S._normal(rng, (len(seqs), hkv, d), "bf16")
+        tv = S._normal(rng, (len(seqs), hkv, d), "bf16")
+        pao.slot_write(kh, vh, tk, tv, np.array(step_slots), bs)
+        H.dev_write(kd, vd, tk, tv, np.array(step_slots))
+    assert pool.stats()["n_copies"] == 5
+    np.testing.assert_array_equal(H.to_host(kd), kh)
+    np.testing.assert_array_equal(H.to_host(vd), vh)
+    tab = np.stack([pool.table(s, cfg.max_blocks_per_seq) for s in seqs])
+    ctx = np.array([pool.seq_len(s) for s in seqs], dtype=np.int32)
+    q = S._normal(rng, (len(seqs), hq, d), "bf16")
+    ref = pao.decode_concat(q, kh, vh, tab, ctx, cfg.scale)
+    for mode in (0, pa.PA_PARTITION_BALANCED, pa.PA_PARTITION_SHARED, 64):
+        got = H.gpu_decode(q, kd, vd, tab, ctx, cfg.scale, None, mode, MFMA)
+        H.assert_close_to_oracle(got, ref, "bf16", f"after copy-on-write, mode {mode}")
