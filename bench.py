@@ -7,6 +7,11 @@ one HIP stream, with every input already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
+NAME is one of the decode workloads (default gqa_bf16) or a beam-search
+workload (beam_bf16, beam_tiny_bf16), whose measured step is its last one:
+that step's copy-on-write block copies (pa_copy_blocks), its slot write and
+the decode of every beam.
+
 Prints ONE JSON line.  `value` is the achieved KV-read bandwidth of the whole
 step (logical KV bytes the step's queries read / step time, in GB/s);
 `tokens_per_s` is the decode throughput (sequences advanced per second, one
@@ -24,6 +29,7 @@ import hashlib
 import json
 import os
 import statistics
+import types
 import sys
 import time
 
@@ -106,6 +112,42 @@ def load_traffic(config, algo_name, partition):
     return rec.get("bytes_per_launch")
 
 
+class BeamLastStep:
+    """The last step of a beam-search workload, seen as a one-step decode
+    workload: the steps before it are replayed (copies and writes) before
+    timing; the timed step is its copy-on-write copies, its slot write and
+    the decode of every beam."""
+
+    def __init__(self, bw):
+        self.bw = bw
+        c = bw.cfg
+        last = bw.steps[-1]
+        self.cfg = types.SimpleNamespace(
+            name=c.name, description=c.description, num_seqs=c.num_seqs,
+            num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads, head_dim=c.head_dim,
+            block_size=c.block_size, num_blocks=c.num_blocks, dtype=c.dtype, scale=c.scale,
+            partition_size=c.partition_size)
+        self.prefill_k, self.prefill_v, self.prefill_slots = bw.prefill_k, bw.prefill_v, \
+            bw.prefill_slots
+        self.earlier_steps = bw.steps[:-1]
+        self.cow = last.cow
+        self.step_k, self.step_v, self.step_slots, self.q = [last.k], [last.v], [last.slots], \
+            [last.q]
+        self._last = last
+
+    def ctx_at(self, s):
+        return self._last.ctx
+
+    def tables_at(self, s):
+        return self._last.tables
+
+    def kv_logical_bytes(self, s):
+        return self.bw.kv_logical_bytes(len(self.bw.steps) - 1)
+
+    def kv_unique_bytes(self, s):
+        return self.bw.kv_unique_bytes(len(self.bw.steps) - 1)
+
+
 def cpu_baseline(w, target_seconds):
     """Time the oracle (slot write of the step's tokens + float64
     concatenate-then-attend) on a bounded prefix of the batch, all cores."""
@@ -116,11 +158,18 @@ def cpu_baseline(w, target_seconds):
                   dtype=w.prefill_k.dtype)
     vh = np.zeros_like(kh)
     pao.slot_write(kh, vh, w.prefill_k, w.prefill_v, w.prefill_slots, c.block_size)
+    for st in getattr(w, "earlier_steps", []):
+        for src, dst in st.cow:
+            pao.copy_block(kh, vh, int(src), int(dst))
+        pao.slot_write(kh, vh, st.k, st.v, st.slots, c.block_size)
+    cow = getattr(w, "cow", [])
     ctx, tab, q = w.ctx_at(0), w.tables_at(0), w.q[0]
     es = 2 if c.dtype == "bf16" else 4
 
     def run(n, threads):
         t = time.perf_counter()
+        for src, dst in cow:
+            pao.copy_block(kh, vh, int(src), int(dst))
         pao.slot_write(kh, vh, w.step_k[0][:n], w.step_v[0][:n], w.step_slots[0][:n],
                        c.block_size)
         pao.decode_concat(q[:n], kh, vh, tab[:n], ctx[:n], c.scale, nthreads=threads)
@@ -174,7 +223,8 @@ def main():
     algo = {"auto": pa.PA_ALGO_AUTO, "vector": pa.PA_ALGO_VECTOR, "mfma": pa.PA_ALGO_MFMA}[args.algo]
 
     log(f"building workload {args.config}")
-    w = S.make_workload(args.config)
+    w = BeamLastStep(S.make_beam_workload(args.config)) if args.config in S.BEAM_CONFIGS \
+        else S.make_workload(args.config)
     c = w.cfg
     tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
 
@@ -189,6 +239,12 @@ def main():
     v_cache = torch.zeros(shape, dtype=tdt, device=dev)
     pa.pa_reshape_and_cache(dev_t(w.prefill_k), dev_t(w.prefill_v), k_cache, v_cache,
                             dev_t(w.prefill_slots))
+    for st in getattr(w, "earlier_steps", []):   # beam workloads: the steps before the last
+        if len(st.cow):
+            pa.pa_copy_blocks(k_cache, v_cache, dev_t(st.cow))
+        pa.pa_reshape_and_cache(dev_t(st.k), dev_t(st.v), k_cache, v_cache, dev_t(st.slots))
+    cow_h = getattr(w, "cow", np.zeros((0, 2), dtype=np.int32))
+    cow = dev_t(cow_h) if len(cow_h) else None
     q = dev_t(w.q[0])
     new_k, new_v = dev_t(w.step_k[0]), dev_t(w.step_v[0])
     slots = dev_t(w.step_slots[0])
@@ -213,6 +269,8 @@ def main():
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
+        if cow is not None:         # the step's copy-on-write copies, then its writes
+            pa.pa_copy_blocks(k_cache, v_cache, cow, stream=stream)
         pa.pa_reshape_and_cache(new_k, new_v, k_cache, v_cache, slots, stream=stream)
         if evs is not None:
             evs[1].record(stream)

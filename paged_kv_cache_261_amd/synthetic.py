@@ -361,3 +361,226 @@ def make_workload(name_or_cfg, num_steps: int = 1, share: bool = True,
                     n_blocks_at=n_blocks_at, prefill_slots=prefill_slots, prefill_k=pk,
                     prefill_v=pv, step_slots=step_slots, step_k=sk, step_v=sv, q=qs,
                     groups=groups if share else [], free_order=free_order)
+
+
+# --------------------------------------------------------------------------
+# Beam-search workload: per-step fork/free churn over shared blocks
+# --------------------------------------------------------------------------
+# Shaped like the beam-search demo of "CS349E 第 7 讲 01_paged_attention.py"
+# (demo 4: a prompt, k candidates that share it and the path they walked
+# together, copy-on-write only when a candidate writes into a shared last
+# block).  The candidates' choices come from a seeded stream, not a model:
+# at step s, new beam j of request r continues old beam parents[s][r][j]
+# (sorted, as a top-k over candidates grouped by parent would order them).
+#
+# Per step, in this order: every new beam forks its parent (reference counts
+# up), every old beam is freed (counts down; a block reaching zero goes back
+# on the free stack, table order), then every new beam appends one token: a
+# fresh block when the position starts a block, else a copy of the last block
+# first when that block is shared.  The block manager below keeps only the
+# bookkeeping the schedule needs (which block ids the tables hold); it moves
+# no data.  Random streams: parents from default_rng(seed); the free stack
+# from default_rng([seed, 3]); prompt K/V of request r from
+# default_rng([seed, 5, r]); step s tokens from default_rng([seed, 6, s]);
+# q of step s from default_rng([seed, 7, s]).
+
+@dataclass(frozen=True)
+class BeamConfig:
+    name: str
+    seed: int
+    num_requests: int
+    beam_width: int
+    prompt_len: int
+    steps: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    dtype: str
+    scale: float
+    description: str
+    partition_size: int = -3
+
+    @property
+    def num_seqs(self) -> int:
+        return self.num_requests * self.beam_width
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return (self.prompt_len + self.steps + self.block_size - 1) // self.block_size
+
+
+BEAM_CONFIGS = {
+    "beam_tiny_bf16": BeamConfig(
+        name="beam_tiny_bf16", seed=11, num_requests=2, beam_width=4, prompt_len=64, steps=32,
+        num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=256,
+        dtype="bf16", scale=1 / math.sqrt(128),
+        description="bf16 beam search, demo size: 2 requests x 4 beams, 64-token prompts, "
+                    "32 steps, block 16, 8 q / 2 kv heads, head_dim 128"),
+    "beam_bf16": BeamConfig(
+        name="beam_bf16", seed=12, num_requests=64, beam_width=4, prompt_len=1024, steps=64,
+        num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=16384,
+        dtype="bf16", scale=1 / math.sqrt(128),
+        description="bf16 beam search: 64 requests x 4 beams, 1024-token prompts, 64 steps, "
+                    "block 16, 32 q / 8 kv heads, head_dim 128"),
+}
+
+
+class _RefPool:
+    """Reference-counted block ids with a LIFO free stack (bookkeeping only)."""
+
+    def __init__(self, free_order, block_size):
+        self.free = [int(x) for x in free_order]
+        self.ref = np.zeros(len(free_order), dtype=np.int64)
+        self.bs = block_size
+        self.tables, self.lens = {}, {}
+        self.next_id = 0
+        self.copies = 0
+
+    def _alloc(self):
+        if not self.free:
+            raise RuntimeError("workload needs more physical blocks than the pool holds")
+        b = self.free.pop()
+        self.ref[b] = 1
+        return b
+
+    def new_seq(self):
+        s = self.next_id
+        self.next_id += 1
+        self.tables[s], self.lens[s] = [], 0
+        return s
+
+    def fork(self, s):
+        t = self.new_seq()
+        self.tables[t] = list(self.tables[s])
+        self.lens[t] = self.lens[s]
+        for b in self.tables[t]:
+            self.ref[b] += 1
+        return t
+
+    def free_seq(self, s):
+        for b in self.tables.pop(s):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        del self.lens[s]
+
+    def append(self, s):
+        """Slot of the token at position len(s); (src, dst) when it copied."""
+        pos, tab, cow = self.lens[s], self.tables[s], None
+        if pos % self.bs == 0:
+            tab.append(self._alloc())
+        else:
+            b = tab[pos // self.bs]
+            if self.ref[b] > 1:
+                nb = self._alloc()
+                self.ref[b] -= 1
+                tab[pos // self.bs] = nb
+                self.copies += 1
+                cow = (b, nb)
+        self.lens[s] = pos + 1
+        return tab[pos // self.bs] * self.bs + pos % self.bs, cow
+
+
+@dataclass
+class BeamStep:
+    parents: np.ndarray      # int [R, k]: old beam each new beam continues
+    tables: np.ndarray       # int32 [R*k, max_blocks] after the step's append (-1 padded)
+    ctx: np.ndarray          # int32 [R*k], including the step's token
+    slots: np.ndarray        # int64 [R*k], slot of the step's token
+    cow: np.ndarray          # int32 [n, 2] (src, dst) copies made before the step's writes
+    k: np.ndarray            # [R*k, Hkv, d]
+    v: np.ndarray
+    q: np.ndarray            # [R*k, Hq, d]
+    used_blocks: int         # blocks held after the step
+    unshared_blocks: int     # blocks the beams would hold without sharing
+
+
+@dataclass
+class BeamWorkload:
+    cfg: BeamConfig
+    free_order: np.ndarray
+    prefill_slots: np.ndarray
+    prefill_k: np.ndarray
+    prefill_v: np.ndarray
+    steps: list
+    n_copies: int
+
+    def kv_logical_bytes(self, s: int) -> int:
+        c = self.cfg
+        es = 2 if c.dtype == "bf16" else 4
+        return int(self.steps[s].ctx.astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * es
+
+    def kv_unique_bytes(self, s: int) -> int:
+        c = self.cfg
+        es = 2 if c.dtype == "bf16" else 4
+        st = self.steps[s]
+        j = np.arange(st.tables.shape[1], dtype=np.int64)[None, :]
+        vis = np.clip(st.ctx.astype(np.int64)[:, None] - j * c.block_size, 0, c.block_size)
+        use = vis > 0
+        best = np.zeros(c.num_blocks, dtype=np.int64)
+        np.maximum.at(best, st.tables[use], vis[use])
+        return int(best.sum()) * c.num_kv_heads * c.head_dim * 2 * es
+
+
+def make_beam_workload(name_or_cfg, with_values: bool = True) -> BeamWorkload:
+    cfg = BEAM_CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
+    R, k, bs, hkv, d = cfg.num_requests, cfg.beam_width, cfg.block_size, cfg.num_kv_heads, \
+        cfg.head_dim
+    rng = np.random.default_rng(cfg.seed)
+    free_order = np.random.default_rng([cfg.seed, 3]).permutation(cfg.num_blocks).astype(np.int32)
+    pool = _RefPool(free_order, bs)
+    sd = storage_dtype(cfg.dtype)
+
+    # prompts: one sequence per request, then k - 1 forks of it
+    beams, pre_slots = [], []
+    for r in range(R):
+        lead = pool.new_seq()
+        pre_slots.extend(pool.append(lead)[0] for _ in range(cfg.prompt_len))
+        beams.append([lead] + [pool.fork(lead) for _ in range(k - 1)])
+    if with_values:
+        pk = np.empty((R * cfg.prompt_len, hkv, d), dtype=sd)
+        pv = np.empty_like(pk)
+        for r in range(R):
+            kr, vr = _draw_tokens([cfg.seed, 5, r], cfg.prompt_len, hkv, d, cfg.dtype)
+            pk[r * cfg.prompt_len:(r + 1) * cfg.prompt_len] = kr
+            pv[r * cfg.prompt_len:(r + 1) * cfg.prompt_len] = vr
+    else:
+        pk = pv = np.zeros((0, hkv, d), dtype=sd)
+
+    steps = []
+    mb = cfg.max_blocks_per_seq
+    for s in range(cfg.steps):
+        parents = np.sort(rng.integers(0, k, size=(R, k)), axis=1)
+        new = [[pool.fork(beams[r][parents[r, j]]) for j in range(k)] for r in range(R)]
+        for r in range(R):
+            for old in beams[r]:
+                pool.free_seq(old)
+        beams = new
+        order = [x for r in range(R) for x in beams[r]]
+        slots, cow = [], []
+        for x in order:
+            slot, c = pool.append(x)
+            slots.append(slot)
+            if c is not None:
+                cow.append(c)
+        tables = np.full((R * k, mb), -1, dtype=np.int32)
+        for i, x in enumerate(order):
+            tables[i, :len(pool.tables[x])] = pool.tables[x]
+        ctx = np.array([pool.lens[x] for x in order], dtype=np.int32)
+        if with_values:
+            kk, vv = _draw_tokens([cfg.seed, 6, s], R * k, hkv, d, cfg.dtype)
+            q = _normal(np.random.default_rng([cfg.seed, 7, s]), (R * k, cfg.num_q_heads, d),
+                        cfg.dtype)
+        else:
+            kk = vv = np.zeros((0, hkv, d), dtype=sd)
+            q = np.zeros((0, cfg.num_q_heads, d), dtype=sd)
+        steps.append(BeamStep(
+            parents=parents, tables=tables, ctx=ctx, slots=np.array(slots, dtype=np.int64),
+            cow=np.array(cow, dtype=np.int32).reshape(-1, 2), k=kk, v=vv, q=q,
+            used_blocks=int((pool.ref > 0).sum()),
+            unshared_blocks=int(sum((pool.lens[x] + bs - 1) // bs for x in order))))
+    return BeamWorkload(cfg=cfg, free_order=free_order,
+                        prefill_slots=np.array(pre_slots, dtype=np.int64), prefill_k=pk,
+                        prefill_v=pv, steps=steps, n_copies=pool.copies)

@@ -139,3 +139,60 @@ def test_bf16_rounding_matches_torch():
 def test_statistics_of_values():
     w = S.make_workload("tiny_f32")
     assert abs(float(w.prefill_k.mean())) < 0.1 and abs(float(w.prefill_k.std()) - 1) < 0.1
+
+
+# --------------------------------------------------------------------------
+# beam-search workload
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["beam_tiny_bf16", "beam_bf16"])
+def test_beam_schedule_matches_oracle_pool(name):
+    """The beam workload's block schedule (tables, slots, copy-on-write pairs,
+    held blocks) equals the oracle pool's when the oracle is driven through
+    the same forks, frees and appends with the same free stack."""
+    from oracle import Pool
+    w = S.make_beam_workload(name, with_values=False)
+    c = w.cfg
+    pool = Pool(c.num_blocks, c.block_size, free_order=w.free_order)
+    beams, slots = [], []
+    for r in range(c.num_requests):
+        lead = pool.seq_new()
+        slots.extend(pool.append(lead)[0] for _ in range(c.prompt_len))
+        beams.append([lead] + [pool.fork(lead) for _ in range(c.beam_width - 1)])
+    np.testing.assert_array_equal(np.array(slots), w.prefill_slots)
+    for st in w.steps:
+        new = [[pool.fork(beams[r][st.parents[r, j]]) for j in range(c.beam_width)]
+               for r in range(c.num_requests)]
+        for r in range(c.num_requests):
+            for old in beams[r]:
+                pool.free(old)
+        beams = new
+        order = [x for r in range(c.num_requests) for x in beams[r]]
+        got_slots, cow = [], []
+        for x in order:
+            slot, src, dst = pool.append(x)
+            got_slots.append(slot)
+            if src >= 0:
+                cow.append((src, dst))
+        np.testing.assert_array_equal(np.array(got_slots), st.slots)
+        np.testing.assert_array_equal(np.array(cow, dtype=np.int32).reshape(-1, 2), st.cow)
+        tab = np.stack([pool.table(x, c.max_blocks_per_seq) for x in order])
+        np.testing.assert_array_equal(tab, st.tables)
+        np.testing.assert_array_equal(np.array([pool.seq_len(x) for x in order]), st.ctx)
+        assert pool.stats()["n_used"] == st.used_blocks
+    assert pool.stats()["n_copies"] == w.n_copies
+
+
+def test_beam_sharing_saves_blocks_and_copies_only_shared_tails():
+    """Demo 4's observations in this schedule: beams hold far fewer blocks
+    than unshared copies would, and copy-on-write copies happen only for a
+    write into a shared, partly filled block (never at a block start)."""
+    w = S.make_beam_workload("beam_tiny_bf16", with_values=False)
+    bs = w.cfg.block_size
+    for st in w.steps:
+        assert st.used_blocks < st.unshared_blocks
+        pos = st.ctx - 1
+        copied = set(int(d) for _, d in st.cow)
+        for i, slot in enumerate(st.slots):
+            if pos[i] % bs == 0:
+                assert slot // bs not in copied
+    assert w.n_copies > 0

@@ -605,3 +605,85 @@ def test_copy_blocks_then_decode_matches_oracle():
     for mode in (0, pa.PA_PARTITION_BALANCED, pa.PA_PARTITION_SHARED, 64):
         got = H.gpu_decode(q, kd, vd, tab, ctx, cfg.scale, None, mode, MFMA)
         H.assert_close_to_oracle(got, ref, "bf16", f"after copy-on-write, mode {mode}")
+
+
+# --------------------------------------------------------------------------
+# beam-search workload: fork/free churn, copy-on-write, diverging tables
+# --------------------------------------------------------------------------
+def run_beam(w, decode_steps=(), modes=(0,)):
+    """Replay a beam workload on the device (copies, slot writes) and on the
+    oracle's pool side by side; decode at the given steps in every mode and
+    compare with the oracle.  Returns the final pools."""
+    c = w.cfg
+    cfg = S.Config(name=c.name, seed=c.seed, num_seqs=c.num_seqs, num_q_heads=c.num_q_heads,
+                   num_kv_heads=c.num_kv_heads, head_dim=c.head_dim, block_size=c.block_size,
+                   num_blocks=c.num_blocks, max_blocks_per_seq=c.max_blocks_per_seq,
+                   dtype=c.dtype, scale=c.scale, description="")
+    kh, vh = H.empty_pool(cfg)
+    kd, vd = H.dev_empty_pool(cfg)
+    pao.slot_write(kh, vh, w.prefill_k, w.prefill_v, w.prefill_slots, c.block_size)
+    H.dev_write(kd, vd, w.prefill_k, w.prefill_v, w.prefill_slots)
+    for s, st in enumerate(w.steps):
+        if len(st.cow):
+            pa.pa_copy_blocks(kd, vd, H.to_dev(st.cow))
+            for src, dst in st.cow:
+                pao.copy_block(kh, vh, int(src), int(dst))
+        pao.slot_write(kh, vh, st.k, st.v, st.slots, c.block_size)
+        H.dev_write(kd, vd, st.k, st.v, st.slots)
+        if s in decode_steps:
+            idx = np.arange(c.num_seqs) if c.num_seqs <= 16 else sample_seqs_ctx(st.ctx, 8)
+            ref = pao.decode_concat(st.q[idx], kh, vh, st.tables[idx], st.ctx[idx], c.scale)
+            for mode in modes:
+                note(f"[gpu parity] {c.name} step {s} mode {mode}")
+                got = H.gpu_decode(st.q, kd, vd, st.tables, st.ctx, c.scale, None, mode, MFMA)
+                H.assert_close_to_oracle(got[idx], ref, c.dtype, f"{c.name} step {s} mode {mode}")
+    return kd, vd, kh, vh
+
+
+def sample_seqs_ctx(ctx, k):
+    rng = np.random.default_rng(98)
+    pick = set(int(x) for x in rng.choice(len(ctx), size=k, replace=False))
+    pick.update({0, len(ctx) - 1})
+    return np.array(sorted(pick))
+
+
+def test_beam_search_workload_small():
+    """The demo-sized beam search (2 requests x 4 beams, 64-token prompts,
+    32 steps): pools stay bit-identical to the oracle's through every
+    copy-on-write, and decode matches the oracle at several steps in every
+    split mode."""
+    w = S.make_beam_workload("beam_tiny_bf16")
+    kd, vd, kh, vh = run_beam(w, decode_steps=(0, 1, 15, 16, 31),
+                              modes=(0, 64, pa.PA_PARTITION_BALANCED, pa.PA_PARTITION_SHARED))
+    np.testing.assert_array_equal(H.to_host(kd), kh)
+    np.testing.assert_array_equal(H.to_host(vd), vh)
+
+
+def test_beam_search_sharing_changes_no_bits():
+    """Demo 4: the k results are the same with sharing and copy-on-write as
+    with every beam holding its own copy of its history."""
+    w = S.make_beam_workload("beam_tiny_bf16")
+    c = w.cfg
+    kd, vd, kh, vh = run_beam(w)
+    st = w.steps[-1]
+    a = H.gpu_decode(st.q, kd, vd, st.tables, st.ctx, c.scale, None, 0, MFMA)
+    # private layout: gather each beam's logical K/V from the oracle pool
+    kl, vl = [], []
+    for i in range(c.num_seqs):
+        pos = np.arange(st.ctx[i])
+        blk = st.tables[i, pos // c.block_size]
+        kl.append(kh[blk, :, pos % c.block_size, :])
+        vl.append(vh[blk, :, pos % c.block_size, :])
+    kc2, vc2, tab2 = H.paginate(kl, vl, c.block_size, c.num_seqs * c.max_blocks_per_seq + 4,
+                                np.random.default_rng(3), c.dtype)
+    b = H.gpu_decode(st.q, H.to_dev(kc2), H.to_dev(vc2), tab2, st.ctx, c.scale, None, 0, MFMA)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_beam_search_workload_full_size():
+    """64 requests x 4 beams, 1024-token prompts, 64 steps: the final step's
+    decode (the launch configuration the benchmark times) matches the
+    oracle on sampled beams."""
+    w = S.make_beam_workload("beam_bf16")
+    run_beam(w, decode_steps=(len(w.steps) - 1,),
+             modes=(w.cfg.partition_size, -1, pa.PA_PARTITION_BALANCED, 0))
