@@ -63,3 +63,37 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale, num_kv_heads, h
                          for i in range(head_dim)])
         out.append(rows)
     return out
+
+
+def prefill(q, cu_seqlens_q, k_pool, v_pool, block_tables, context_lens, scale, num_kv_heads,
+            head_dim, block_size, is_bf16=False):
+    """Causal prefill of a packed chunk batch: q nested lists [total_q][Hq][d];
+    the chunk of sequence b is rows cu[b]..cu[b+1]-1, the last positions of
+    its context_lens[b] tokens; row r at position p sees positions 0..p.
+    Returns [total_q][Hq][d] floats."""
+    out = [None] * len(q)
+    for b, n in enumerate(context_lens):
+        q0, q1 = cu_seqlens_q[b], cu_seqlens_q[b + 1]
+        for r in range(q1 - q0):
+            p = n - (q1 - q0) + r
+            hq = len(q[q0 + r])
+            group = hq // num_kv_heads
+            rows = []
+            for h in range(hq):
+                g = h // group
+                qh = [bf16_bits_to_float(int(x)) if is_bf16 else float(x) for x in q[q0 + r][h]]
+                bases = []
+                for pos in range(p + 1):
+                    logical, offset = divmod(pos, block_size)
+                    physical = block_tables[b][logical]
+                    bases.append(((physical * num_kv_heads + g) * block_size + offset) * head_dim)
+                scores = [scale * math.fsum(qh[i] * element(k_pool, base + i, is_bf16)
+                                            for i in range(head_dim)) for base in bases]
+                top = max(scores)
+                weights = [math.exp(s - top) for s in scores]
+                total = math.fsum(weights)
+                rows.append([math.fsum(w * element(v_pool, base + i, is_bf16)
+                                       for w, base in zip(weights, bases)) / total
+                             for i in range(head_dim)])
+            out[q0 + r] = rows
+    return out

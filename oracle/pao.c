@@ -644,3 +644,85 @@ int pao_decode_partitioned_f64(double *out, const void *q, const void *k_cache,
     }
     return failed ? PAO_E_ARG : PAO_OK;
 }
+
+/* (4) Prefill: for sequence b the chunk's n_b = cu[b+1] - cu[b] query rows
+ * are the last n_b positions of a sequence of n = context_lens[b] tokens
+ * whose K/V (the chunk's included) are already in the cache ([P3] section
+ * B.2: a prefill batch is packed by cu_seqlens_q; [P2] demo 1 prefills a
+ * prompt, then decodes).  Row r of the chunk, at position p = n - n_b + r,
+ * attends causally over positions 0..p:
+ *   s_j = scale * sum_i q[r][h][i] K[j][i],   j <= p
+ *   o[r][h][i] = (sum_{j<=p} exp(s_j - m) V[j][i]) / sum_{j<=p} exp(s_j - m),
+ * m = max_{j<=p} s_j.  The gather is the same as in (1). */
+int pao_prefill_concat_f64(double *out, const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *block_tables,
+                           const int32_t *cu_seqlens_q, const int32_t *context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int num_blocks, int block_size, int max_blocks_per_seq,
+                           double scale, int dtype, int nthreads)
+{
+    decode_args a = {q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                     max_blocks_per_seq, dtype, scale};
+    int rc = check_args(&a, out);
+    if (rc != PAO_OK || num_seqs == 0) return rc;
+    if (!cu_seqlens_q || cu_seqlens_q[0] != 0) return PAO_E_ARG;
+    for (int b = 0; b < num_seqs; b++) {
+        int nq = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+        if (nq < 0 || nq > context_lens[b]) return PAO_E_ARG;
+    }
+    set_threads(nthreads);
+    const int G = num_q_heads / num_kv_heads;
+    const int d = head_dim;
+    const long n_pairs = (long)num_seqs * num_kv_heads;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long pair = 0; pair < n_pairs; pair++) {
+        int b = (int)(pair / num_kv_heads);
+        int g = (int)(pair % num_kv_heads);
+        int n = context_lens[b];
+        int q0 = cu_seqlens_q[b], nq = cu_seqlens_q[b + 1] - q0;
+        if (nq == 0) continue;
+        double *K = (double *)malloc((size_t)n * d * sizeof(double));
+        double *V = (double *)malloc((size_t)n * d * sizeof(double));
+        double *s = (double *)malloc((size_t)n * sizeof(double));
+        if (!K || !V || !s) {
+            free(K); free(V); free(s);
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        for (int j = 0; j < n; j++)
+            for (int i = 0; i < d; i++) {
+                K[(size_t)j * d + i] = load_elem(k_cache, pool_index(&a, b, g, j, i), dtype);
+                V[(size_t)j * d + i] = load_elem(v_cache, pool_index(&a, b, g, j, i), dtype);
+            }
+        for (int r = 0; r < nq; r++) {
+            int p = n - nq + r;               /* position of chunk row r */
+            for (int h = g * G; h < (g + 1) * G; h++) {
+                size_t qo = ((size_t)(q0 + r) * num_q_heads + h) * d;
+                double m = -INFINITY;
+                for (int j = 0; j <= p; j++) {
+                    double acc = 0.0;
+                    for (int i = 0; i < d; i++)
+                        acc += load_elem(q, qo + i, dtype) * K[(size_t)j * d + i];
+                    s[j] = scale * acc;
+                    if (s[j] > m) m = s[j];
+                }
+                double L = 0.0;
+                for (int j = 0; j <= p; j++) {
+                    s[j] = exp(s[j] - m);
+                    L += s[j];
+                }
+                for (int i = 0; i < d; i++) {
+                    double acc = 0.0;
+                    for (int j = 0; j <= p; j++) acc += s[j] * V[(size_t)j * d + i];
+                    out[qo + i] = acc / L;
+                }
+            }
+        }
+        free(K); free(V); free(s);
+    }
+    return failed ? PAO_E_ARG : PAO_OK;
+}

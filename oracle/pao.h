@@ -11,7 +11,9 @@
  *     copy-on-write and free;
  *   - the slot write that places one token's K/V at its physical slot;
  *   - decode attention in float64, in three forms (concatenate-then-attend,
- *     blockwise with one global softmax, partitioned with a log-sum-exp merge).
+ *     blockwise with one global softmax, partitioned with a log-sum-exp merge);
+ *   - prefill attention in float64: a chunk of new tokens per sequence, each
+ *     attending causally over the cache up to its own position.
  *
  * Sources (cited by page title and the named part of the page):
  *   [P1] "PagedAttention实现" (ainanfeng.cn project page): KVBlock, PageTable,
@@ -21,10 +23,11 @@
  *        blockwise attention, sharing and copy-on-write" (lecture script):
  *        demo 1 (block-table growth), demo 2 (paged = contiguous; paper eq. 4
  *        blockwise attention), demo 3 (parallel sampling, copy-on-write),
- *        demo 4 (beam search).
+ *        demo 4 (beam search); demo 1's prefill of a 7-token prompt.
  *   [P3] "04 - Paged Attention 实现进度": section A.2 (five components,
- *        block_tables / slot_mapping shapes), section B.2 (Context fields),
- *        section B.3 (block size 16).
+ *        block_tables / slot_mapping shapes), section B.2 (Context fields,
+ *        cu_seqlens_q / cu_seqlens_k of a prefill batch), section B.3 (block
+ *        size 16).
  *
  * Every function returns a status: 0 on success, a negative PAO_E* code on
  * error.  The oracle never aborts on bad input.
@@ -128,6 +131,24 @@ int pao_decode_partitioned_f64(double *out, const void *q, const void *k_cache,
                                int num_kv_heads, int head_dim, int num_blocks,
                                int block_size, int max_blocks_per_seq, double scale,
                                int dtype, int partition_size, int nthreads);
+
+/* ------------------------------------------------------------------------ */
+/* Prefill attention over the paged cache in float64 (a chunk of new tokens  */
+/* per sequence, causal).                                                      */
+/*   out  [total_q][num_q_heads][head_dim] float64                           */
+/*   q    [total_q][num_q_heads][head_dim] in dtype: the chunk of sequence b  */
+/*        is rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1                     */
+/*   context_lens [num_seqs]: tokens in the cache after the chunk's write     */
+/* The chunk's n_b tokens are the last n_b positions of the sequence: row r  */
+/* of the chunk sits at position p = context_lens[b] - n_b + r and attends   */
+/* over positions 0 .. p (its own included).  n_b == 1 is decode.            */
+/* ------------------------------------------------------------------------ */
+int pao_prefill_concat_f64(double *out, const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *block_tables,
+                           const int32_t *cu_seqlens_q, const int32_t *context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int num_blocks, int block_size, int max_blocks_per_seq,
+                           double scale, int dtype, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -56,6 +56,7 @@ def load_library():
         "pao_decode_concat_f64": (I, [P, P, P, P, P, P] + [I] * 7 + [C.c_double, I, I]),
         "pao_decode_blockwise_f64": (I, [P, P, P, P, P, P] + [I] * 7 + [C.c_double, I, I]),
         "pao_decode_partitioned_f64": (I, [P, P, P, P, P, P] + [I] * 7 + [C.c_double, I, I, I]),
+        "pao_prefill_concat_f64": (I, [P] * 7 + [I] * 7 + [C.c_double, I, I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -195,6 +196,29 @@ def _decode(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, dty
                                block_tables.shape[1], float(scale), int(dtype), *extra,
                                int(nthreads))
     _check(rc, fn_name)
+    return out
+
+
+def prefill_concat(q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens, scale,
+                   nthreads=0):
+    """Causal prefill of a packed chunk batch (q [total_q, Hq, d]); float64 out."""
+    lib = load_library()
+    q = np.ascontiguousarray(q)
+    block_tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    tq, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    b = context_lens.shape[0]
+    assert d == d2 and v_cache.shape == k_cache.shape
+    assert block_tables.shape[0] == b and cu.shape == (b + 1,) and cu[-1] == tq
+    out = np.zeros((tq, hq, d), dtype=np.float64)
+    rc = lib.pao_prefill_concat_f64(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(block_tables), _ptr(cu), _ptr(context_lens), b, hq, hkv,
+                                    d, nb, bs, block_tables.shape[1], float(scale),
+                                    int(_dtype_code(q)), int(nthreads))
+    _check(rc, "pao_prefill_concat_f64")
     return out
 
 

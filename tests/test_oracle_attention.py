@@ -294,3 +294,122 @@ def test_slot_write_rejects_repeats_and_out_of_range():
     assert (k == 0).all()
     pao.slot_write(k, v, tok, tok, np.array([-1, 7]), 2)      # negative: padding, skipped
     assert k.sum() == 3 and k[3, 0, 1].sum() == 3
+
+
+# --------------------------------------------------------------------------
+# prefill (a chunk of new tokens per sequence, causal over the paged cache)
+# --------------------------------------------------------------------------
+def prefill_case(rng, chunks, prefixes, hq, hkv, d, bs, dtype):
+    """Per sequence: a cached prefix plus a chunk of new tokens (all in the
+    pool); q rows for the chunk, packed.  Returns q, cu, ctx, paged pool,
+    tables and the logical K/V lists."""
+    ctxs = [p + c for p, c in zip(prefixes, chunks)]
+    q = S._normal(rng, (sum(chunks), hq, d), dtype)
+    kl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    vl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    nb = sum((n + bs - 1) // bs for n in ctxs) + 3
+    kc, vc, tab = H.paginate(kl, vl, bs, nb, rng, dtype)
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    return q, cu, np.array(ctxs, dtype=np.int32), kc, vc, tab, kl, vl
+
+
+def sdpa_prefill_reference(q, cu, kl, vl, scale, dtype):
+    """torch SDPA in float64 on contiguous K/V with the causal mask aligned to
+    the end of the sequence (chunk row r sees keys 0 .. n - nq + r)."""
+    out = np.zeros(q.shape, dtype=np.float64)
+    qf = H.to_float(q, dtype)
+    for b in range(len(kl)):
+        q0, q1 = cu[b], cu[b + 1]
+        nq, n = q1 - q0, kl[b].shape[0]
+        if nq == 0:
+            continue
+        hq, hkv = q.shape[1], kl[b].shape[1]
+        K = torch.from_numpy(H.to_float(kl[b], dtype)).permute(1, 0, 2)
+        V = torch.from_numpy(H.to_float(vl[b], dtype)).permute(1, 0, 2)
+        K = K.repeat_interleave(hq // hkv, dim=0).contiguous()
+        V = V.repeat_interleave(hq // hkv, dim=0).contiguous()
+        Q = torch.from_numpy(qf[q0:q1]).permute(1, 0, 2).contiguous()      # [Hq, nq, d]
+        rows = torch.arange(nq)[:, None] + (n - nq)
+        mask = torch.arange(n)[None, :] <= rows                            # [nq, n]
+        o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask,
+                                                             scale=scale)
+        out[q0:q1] = o.permute(1, 0, 2).numpy()
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("hq,hkv,d,bs", [(4, 4, 16, 4), (8, 2, 32, 16), (6, 3, 8, 1)])
+def test_prefill_matches_sdpa_with_causal_mask(dtype, hq, hkv, d, bs):
+    rng = np.random.default_rng(hq + d + bs)
+    chunks, prefixes = [1, 7, 16, 33, 5], [0, 9, 0, 40, 100]
+    q, cu, ctx, kc, vc, tab, kl, vl = prefill_case(rng, chunks, prefixes, hq, hkv, d, bs, dtype)
+    got = pao.prefill_concat(q, kc, vc, tab, cu, ctx, 0.3)
+    ref = sdpa_prefill_reference(q, cu, kl, vl, 0.3, dtype)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_whole_prompt_prefill_matches_is_causal():
+    """A chunk that is the whole sequence is ordinary causal self-attention."""
+    rng = np.random.default_rng(5)
+    n, hq, d = 37, 4, 16
+    q, cu, ctx, kc, vc, tab, kl, vl = prefill_case(rng, [n], [0], hq, hq, d, 4, "f32")
+    got = pao.prefill_concat(q, kc, vc, tab, cu, ctx, 0.25)
+    Q = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2).contiguous()
+    K = torch.from_numpy(kl[0].astype(np.float64)).permute(1, 0, 2).contiguous()
+    V = torch.from_numpy(vl[0].astype(np.float64)).permute(1, 0, 2).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=0.25)
+    np.testing.assert_allclose(got, ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_matches_brute_force(dtype, seed):
+    rng = np.random.default_rng(2000 + seed)
+    n_seqs = int(rng.integers(1, 4))
+    hkv = int(rng.integers(1, 3))
+    hq = hkv * int(rng.integers(1, 3))
+    d = int(rng.integers(1, 7))
+    bs = int(rng.choice([1, 2, 4]))
+    chunks = [int(x) for x in rng.integers(0, 6, n_seqs)]
+    prefixes = [int(x) for x in rng.integers(0, 10, n_seqs)]
+    chunks = [c if c + p > 0 else 1 for c, p in zip(chunks, prefixes)]
+    q, cu, ctx, kc, vc, tab, kl, vl = prefill_case(rng, chunks, prefixes, hq, hkv, d, bs, dtype)
+    got = pao.prefill_concat(q, kc, vc, tab, cu, ctx, 0.5)
+    ref = brute.prefill(q.tolist(), cu.tolist(), kc.ravel().tolist(), vc.ravel().tolist(),
+                        tab.tolist(), ctx.tolist(), 0.5, hkv, d, bs, is_bf16=(dtype == "bf16"))
+    np.testing.assert_allclose(got, np.array(ref).reshape(got.shape), rtol=0, atol=1e-12)
+
+
+def test_prefill_rows_are_decodes_of_truncated_contexts():
+    """Row r of a chunk (position p) is the decode of a query over the first
+    p + 1 tokens; a chunk of one token is decode itself (bit for bit)."""
+    rng = np.random.default_rng(9)
+    chunks, prefixes = [5, 1, 12], [20, 31, 0]
+    q, cu, ctx, kc, vc, tab, kl, vl = prefill_case(rng, chunks, prefixes, 8, 2, 32, 8, "bf16")
+    got = pao.prefill_concat(q, kc, vc, tab, cu, ctx, 0.2)
+    for b in range(3):
+        for r in range(chunks[b]):
+            row = cu[b] + r
+            p = ctx[b] - chunks[b] + r
+            one = pao.decode_concat(q[row:row + 1], kc, vc, tab[b:b + 1], np.array([p + 1]), 0.2)
+            if chunks[b] == 1:
+                np.testing.assert_array_equal(got[row], one[0])
+            else:
+                assert np.abs(got[row] - one[0]).max() <= 1e-13
+
+
+def test_prefill_paged_equals_contiguous_for_every_block_size():
+    rng = np.random.default_rng(10)
+    chunks, prefixes = [9, 30], [50, 3]
+    ctxs = [p + c for p, c in zip(prefixes, chunks)]
+    q = S._normal(rng, (sum(chunks), 4, 16), "f32")
+    kl = [S._normal(rng, (n, 2, 16), "f32") for n in ctxs]
+    vl = [S._normal(rng, (n, 2, 16), "f32") for n in ctxs]
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    outs = []
+    for bs in BLOCK_SIZES:
+        nb = sum((n + bs - 1) // bs for n in ctxs) + 2
+        kc, vc, tab = H.paginate(kl, vl, bs, nb, np.random.default_rng(bs), "f32")
+        outs.append(pao.prefill_concat(q, kc, vc, tab, cu, np.array(ctxs), 0.25))
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
