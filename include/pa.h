@@ -136,6 +136,36 @@ int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int
                    void *stream);
 
 /*
+ * Paged prefill ("04 - Paged Attention 实现进度", section B.2: a prefill batch
+ * is packed by cu_seqlens_q; "CS349E 第 7 讲 01_paged_attention.py", demo 1
+ * prefills a prompt before decoding, demo 2 / paper eq. 4 for the softmax over
+ * the paged cache).  Sequence b contributes a chunk of n_b = cu_seqlens_q[b+1]
+ * - cu_seqlens_q[b] query rows: the last n_b positions of its
+ * context_lens[b] tokens, whose K/V must already be in the cache (write them
+ * with pa_reshape_and_cache first).  Row r of the chunk, at position
+ * p = context_lens[b] - n_b + r, attends causally over positions 0..p:
+ *     out[row][h][:] = sum_{j<=p} softmax_j(scale * q[row][h] . k_j) v_j
+ * with query head h reading KV head h / (num_q_heads / num_kv_heads).  A
+ * chunk of one row is decode; a chunk that is the whole sequence is ordinary
+ * causal prefill; anything between is chunked prefill over a cached prefix.
+ *
+ *   out, q         [total_q][num_q_heads][head_dim]  (total_q = cu_seqlens_q[num_seqs])
+ *   cu_seqlens_q   [num_seqs + 1] int32, device, cu_seqlens_q[0] = 0, non-decreasing
+ *   context_lens   [num_seqs] int32, device, n_b <= context_lens[b] <= max_context_len
+ *   block_tables, k_cache, v_cache   as for pa_decode
+ *   max_q_len      an upper bound of every n_b (sizes the grid)
+ *
+ * Supported: dtype PA_BF16, head_dim 128, block_size >= 16, group size <= 16
+ * (the matrix-core tile); other shapes return PA_ERR_UNSUPPORTED.  Rows
+ * with n_b = 0 produce nothing.  Asynchronous on `stream`, no workspace.
+ */
+int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+               const int32_t *block_tables, const int32_t *cu_seqlens_q,
+               const int32_t *context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+               int head_dim, int num_blocks, int block_size, int max_blocks_per_seq,
+               int max_context_len, int max_q_len, float scale, int dtype, void *stream);
+
+/*
  * Partition mode the library uses when pa_decode / pa_decode_partitions get
  * partition_size == PA_PARTITION_AUTO for these sizes and PA_ALGO_AUTO:
  * 0 (single pass, no workspace), PA_PARTITION_BALANCED, or a multiple of

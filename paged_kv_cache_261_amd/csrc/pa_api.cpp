@@ -297,6 +297,51 @@ int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+               const int32_t *block_tables, const int32_t *cu_seqlens_q,
+               const int32_t *context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+               int head_dim, int num_blocks, int block_size, int max_blocks_per_seq,
+               int max_context_len, int max_q_len, float scale, int dtype, void *stream) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+        max_blocks_per_seq <= 0 || max_context_len < 0 || max_q_len < 0 ||
+        num_q_heads % num_kv_heads)
+        return PA_ERR_SHAPE;
+    if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || !block_size_ok(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (!balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads))
+        return PA_ERR_UNSUPPORTED;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size ||
+        max_q_len > max_context_len)
+        return PA_ERR_SHAPE;
+    if (num_seqs == 0 || max_q_len == 0) return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !context_lens)
+        return PA_ERR_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_ALIGN;
+    pa::PrefillParams p{};
+    p.out = out;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.context_lens = context_lens;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_q_heads / num_kv_heads;
+    p.num_blocks = num_blocks;
+    p.log2_block = ilog2(block_size);
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_context_len = max_context_len;
+    const int rows_per_wave = 32 / p.group;
+    p.units_per_seq = (max_q_len + rows_per_wave - 1) / rows_per_wave;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    if ((int64_t)num_seqs * num_kv_heads * p.units_per_seq > 0x7fffffff) return PA_ERR_SHAPE;
+    const hipError_t e = pa::launch_prefill(p, (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 int pa_decode_auto_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_context_len, int dtype) {
     if (!block_size_ok(block_size)) return 0;

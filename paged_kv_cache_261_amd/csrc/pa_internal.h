@@ -89,6 +89,26 @@ struct SharedParams {
     float *ws_acc;            // [W][2][32][128]
 };
 
+struct PrefillParams {
+    void *out;                 // [total_q][Hq][D]
+    const void *q;             // [total_q][Hq][D]
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *cu_seqlens_q;   // [B + 1]
+    const int32_t *context_lens;   // [B], after the chunk's write
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int group;
+    int num_blocks;
+    int log2_block;
+    int max_blocks_per_seq;
+    int max_context_len;
+    int units_per_seq;         // ceil(max_q_len / rows per wavefront)
+    float scale_log2;
+};
+
 // Query-head columns of one shared-prefix wavefront: two groups of 16.
 constexpr int kMaxCols = 32;
 
@@ -133,6 +153,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // Launchers: validate nothing (pa_api.cpp does), enqueue, return hipError_t.
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int num_pairs,
                               int num_blocks, int64_t block_bytes, hipStream_t stream);
 hipError_t launch_cache_write(const void *k, const void *v, void *k_cache, void *v_cache,

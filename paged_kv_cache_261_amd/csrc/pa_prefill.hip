@@ -1,0 +1,126 @@
+// pa_prefill.hip -- paged prefill: a chunk of new tokens per sequence, each
+// attending causally over the paged cache up to its own position.
+//
+// What it computes ("04 - Paged Attention 实现进度", section B.2: a prefill
+// batch is packed by cu_seqlens_q; "CS349E 第 7 讲 01_paged_attention.py",
+// demo 1 prefills a prompt before decoding; demo 2 / paper eq. 4 for the
+// per-query softmax over the paged cache): the chunk of sequence b is q rows
+// cu[b] .. cu[b+1]-1, the last n_b positions of its context_lens[b] tokens
+// (already written through slot_mapping); row r at position
+// p = context_lens[b] - n_b + r attends over positions 0..p.
+//
+// How (matrix cores; bf16, head_dim 128, block_size >= 16, group size
+// G <= 16): one wavefront serves 32 query-head columns of one KV head -- the
+// G heads of TPU = 32 / G consecutive chunk rows (two 16-column groups that
+// share every K/V load) -- and walks the keys 0 .. (its last row's position)
+// in 16-token tiles with the tile step of pa_mfma_tile.h; a column's causal
+// limit is its row's position, so the last tiles are partly masked per
+// column.  Wavefronts of one (sequence, KV head) stream the same K/V tiles
+// close together in time, so the repeats are served by L2.
+#include "pa_mfma_tile.h"
+
+namespace pa {
+
+constexpr int kPrefillCols = 32;
+
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ tables,
+                         const int32_t *__restrict__ cu_q, const int32_t *__restrict__ ctx_lens,
+                         void *__restrict__ out) {
+    const PrefillParams &p = args;
+    const int lane = threadIdx.x;
+    const Lane ln{lane & 15, lane >> 4};
+    const int G = p.group;
+    const int TPU = kPrefillCols / G;                       // chunk rows per wavefront
+    // unit = (u fastest, then KV head g, then sequence b); XCD-aware order
+    const int unit = xcd_remap(blockIdx.x, gridDim.x);
+    const int u = unit % p.units_per_seq;
+    const int g = (unit / p.units_per_seq) % p.num_kv_heads;
+    const int b = unit / (p.units_per_seq * p.num_kv_heads);
+    const int q0 = __builtin_amdgcn_readfirstlane(cu_q[b]);
+    const int nq = __builtin_amdgcn_readfirstlane(cu_q[b + 1]) - q0;
+    const int r0 = u * TPU;                                 // first chunk row of the unit
+    if (r0 >= nq) return;
+    const int n = __builtin_amdgcn_readfirstlane(clamp_ctx(ctx_lens[b], p.max_context_len));
+    const int first_pos = n - nq;                           // position of chunk row 0
+    const int r_end = min(nq, r0 + TPU);
+    const int kmax = first_pos + r_end;                     // keys 0 .. kmax-1
+    if (kmax <= 0) return;
+
+    // this lane's columns: column cg * 16 + row16 = head hj of chunk row r
+    int ncol[2], rowid[2], head[2];
+    bool ok[2];
+    bf16x8 qv[2][4];
+    Acc a[2];
+#pragma unroll
+    for (int cg = 0; cg < 2; cg++) {
+        const int col = cg * 16 + ln.row16;
+        const int r = r0 + col / G;
+        head[cg] = g * G + col % G;
+        ok[cg] = col / G < TPU && r < r_end;
+        rowid[cg] = q0 + r;
+        ncol[cg] = ok[cg] ? first_pos + r + 1 : 0;           // keys 0 .. its position
+        const char *qrow = (const char *)p.q +
+                           (((size_t)(ok[cg] ? rowid[cg] : q0) * p.num_q_heads +
+                             (ok[cg] ? head[cg] : 0)) * kD + 8 * ln.grp) * 2;
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            u32x4 raw = *(const u32x4 *)(qrow + 64 * kk);
+            if (!ok[cg]) raw = (u32x4){0u, 0u, 0u, 0u};
+            qv[cg][kk] = __builtin_bit_cast(bf16x8, raw);
+        }
+        acc_init(a[cg]);
+    }
+
+    const char *kbase = (const char *)p.k_cache;
+    const char *vbase = (const char *)p.v_cache;
+    const int32_t *table = tables + (size_t)b * p.max_blocks_per_seq;
+    const int log2bs = p.log2_block;
+    const int bs_mask = (1 << log2bs) - 1;
+    const int ntiles = (kmax + kTile - 1) / kTile;
+    auto phys_of = [&](int t) -> int { return table[(min(t, ntiles - 1) * kTile) >> log2bs]; };
+    auto issue = [&](int t, int phys, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+        const bool in = t < ntiles && (unsigned)phys < (unsigned)p.num_blocks;
+        const int rows = in ? min(kTile, kmax - t * kTile) : 0;
+        const size_t off = ((((size_t)(in ? phys : 0) * p.num_kv_heads + g) << log2bs) +
+                            ((t * kTile) & bs_mask)) * (size_t)kRowBytes;
+        load_tile_rows(kbase, vbase, off, rows, ln, kr, vr);
+    };
+    u32x4 kr[2][4], vr[2][4];
+    int phys_next = phys_of(0);
+    issue(0, phys_next, kr[0], vr[0]);
+    phys_next = phys_of(1);
+    for (int t0 = 0; t0 < ntiles; t0 += 2) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int t = t0 + j;
+            if (t >= ntiles) break;
+            issue(t + 1, phys_next, kr[j ^ 1], vr[j ^ 1]);
+            phys_next = phys_of(t + 2);
+            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the wait
+            if ((unsigned)table[(t * kTile) >> log2bs] < (unsigned)p.num_blocks) {
+#pragma unroll
+                for (int cg = 0; cg < 2; cg++)
+                    tile_update<true>(kr[j], vr[j], qv[cg], ncol[cg] - t * kTile, p.scale_log2,
+                                      a[cg], ln);
+            }
+        }
+    }
+#pragma unroll
+    for (int cg = 0; cg < 2; cg++) {
+        acc_finish(a[cg]);
+        if (ok[cg])
+            store_row((char *)out + ((size_t)rowid[cg] * p.num_q_heads + head[cg]) * kD * 2,
+                      a[cg], ln);
+    }
+}
+
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
+    const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads * p.units_per_seq;
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL(prefill_mfma_kernel, dim3((unsigned)units), dim3(kWave), 0, stream, p,
+                       p.block_tables, p.cu_seqlens_q, p.context_lens, p.out);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -37,6 +37,7 @@ def _load():
     sig = {
         "pa_reshape_and_cache": (I, [P, P, P, P, P, I, I, I, I, I, I, P]),
         "pa_copy_blocks": (I, [P, P, P, I, I, I, I, I, I, P]),
+        "pa_prefill": (I, [P] * 7 + [I] * 9 + [F, I, P]),
         "pa_decode_auto_partition": (I, [I, I, I, I, I, I, I]),
         "pa_decode_workspace_size": (SZ, [I, I, I, I, I, I, I, I]),
         "pa_decode": (I, [P] * 6 + [I] * 8 + [F, I, P, SZ, I, I, P]),
@@ -100,6 +101,29 @@ def pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, stream=None):
                                     _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"),
                                     t, hkv, d, nb, bs, dt, _stream(k, stream)),
            "pa_reshape_and_cache")
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens,
+               max_context_len, max_q_len, scale, stream=None):
+    """Causal prefill of a packed chunk batch q [total_q, Hq, d] over the paged
+    cache (the chunk's K/V already written); out has q's shape."""
+    tq, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    b = context_lens.shape[0]
+    if out.shape != q.shape or d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("q/out/cache shapes disagree")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_q.shape != (b + 1,):
+        raise ValueError("cu_seqlens_q must be int32 [num_seqs + 1]")
+    if context_lens.dtype != torch.int32 or block_tables.dtype != torch.int32:
+        raise ValueError("context_lens and block_tables must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    _check(lib.pa_prefill(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                          _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+                          _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(context_lens, "context_lens"),
+                          b, hq, hkv, d, nb, bs, block_tables.shape[1], int(max_context_len),
+                          int(max_q_len), float(scale), dtype_code(q), _stream(q, stream)),
+           "pa_prefill")
 
 
 def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):

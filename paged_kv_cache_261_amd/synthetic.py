@@ -584,3 +584,122 @@ def make_beam_workload(name_or_cfg, with_values: bool = True) -> BeamWorkload:
     return BeamWorkload(cfg=cfg, free_order=free_order,
                         prefill_slots=np.array(pre_slots, dtype=np.int64), prefill_k=pk,
                         prefill_v=pv, steps=steps, n_copies=pool.copies)
+
+
+# --------------------------------------------------------------------------
+# Prefill workload: a chunk of new tokens per sequence over a cached prefix
+# --------------------------------------------------------------------------
+# Each sequence has a cached prefix (its K/V written before the measured
+# step) and a chunk of new tokens: the measured step writes the chunk's K/V
+# through slot_mapping and runs causal prefill for the chunk's queries.
+# Draw order from default_rng(seed): prefix lengths, chunk lengths, q.  Free
+# stack from default_rng([seed, 3]); blocks are taken sequence by sequence in
+# position order.  Prefix K/V of sequence b from default_rng([seed, 5, b]),
+# chunk K/V from default_rng([seed, 6, b]).
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    seed: int
+    num_seqs: int
+    prefix_rule: tuple          # ("uniform", lo, hi) | ("fixed", [..])
+    chunk_rule: tuple           # ("const", n) | ("fixed", [..])
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    dtype: str
+    scale: float
+    description: str
+
+
+PREFILL_CONFIGS = {
+    "prefill_bf16": PrefillConfig(
+        name="prefill_bf16", seed=21, num_seqs=16, prefix_rule=("uniform", 0, 1536),
+        chunk_rule=("const", 512), num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+        num_blocks=4096, max_blocks_per_seq=128, dtype="bf16", scale=1 / math.sqrt(128),
+        description="bf16 chunked prefill: 16 sequences, 512-token chunks over cached prefixes "
+                    "U[0,1536], 32 q / 8 kv heads, head_dim 128, block 16"),
+}
+
+
+@dataclass
+class PrefillWorkload:
+    cfg: PrefillConfig
+    prefix_lens: np.ndarray
+    chunk_lens: np.ndarray
+    ctx: np.ndarray             # prefix + chunk
+    cu_seqlens_q: np.ndarray    # [B + 1]
+    tables: np.ndarray
+    prefix_slots: np.ndarray
+    prefix_k: np.ndarray
+    prefix_v: np.ndarray
+    chunk_slots: np.ndarray
+    chunk_k: np.ndarray
+    chunk_v: np.ndarray
+    q: np.ndarray               # [total_q, Hq, d]
+
+    def flops(self) -> int:
+        """Multiply-adds x 2 of the causal prefill: 4 d Hq per (query row, key)."""
+        c = self.cfg
+        keys = 0
+        for p, n in zip(self.prefix_lens, self.chunk_lens):
+            keys += int(n) * int(p) + int(n) * (int(n) + 1) // 2
+        return 4 * c.head_dim * c.num_q_heads * keys
+
+    def kv_bytes(self) -> int:
+        c = self.cfg
+        es = 2 if c.dtype == "bf16" else 4
+        return int(self.ctx.astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * es
+
+
+def _lengths(rule, rng, n):
+    if rule[0] == "fixed":
+        return np.asarray(rule[1], dtype=np.int32)
+    if rule[0] == "const":
+        return np.full(n, rule[1], dtype=np.int32)
+    if rule[0] == "uniform":
+        return rng.integers(rule[1], rule[2] + 1, size=n).astype(np.int32)
+    raise ValueError(rule)
+
+
+def make_prefill_workload(name_or_cfg) -> PrefillWorkload:
+    cfg = PREFILL_CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
+    B, bs, hkv, d = cfg.num_seqs, cfg.block_size, cfg.num_kv_heads, cfg.head_dim
+    rng = np.random.default_rng(cfg.seed)
+    prefix = _lengths(cfg.prefix_rule, rng, B)
+    chunk = _lengths(cfg.chunk_rule, rng, B)
+    ctx = (prefix + chunk).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    q = _normal(rng, (int(cu[-1]), cfg.num_q_heads, d), cfg.dtype)
+    free = _FreeStack(np.random.default_rng([cfg.seed, 3]).permutation(cfg.num_blocks))
+    if int(((ctx + bs - 1) // bs).max()) > cfg.max_blocks_per_seq:
+        raise ValueError("max_blocks_per_seq too small")
+    tables = np.full((B, cfg.max_blocks_per_seq), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range((int(ctx[b]) + bs - 1) // bs):
+            tables[b, i] = free.pop()
+
+    def slots(b, lo, hi):
+        pos = np.arange(lo, hi, dtype=np.int64)
+        return tables[b, pos // bs].astype(np.int64) * bs + pos % bs
+
+    sd = storage_dtype(cfg.dtype)
+    pk, pv, ck, cv, ps, cs = [], [], [], [], [], []
+    for b in range(B):
+        k, v = _draw_tokens([cfg.seed, 5, b], int(prefix[b]), hkv, d, cfg.dtype)
+        pk.append(k)
+        pv.append(v)
+        ps.append(slots(b, 0, int(prefix[b])))
+        k, v = _draw_tokens([cfg.seed, 6, b], int(chunk[b]), hkv, d, cfg.dtype)
+        ck.append(k)
+        cv.append(v)
+        cs.append(slots(b, int(prefix[b]), int(ctx[b])))
+    cat = lambda xs, shape: np.concatenate(xs) if xs else np.zeros(shape, dtype=sd)  # noqa: E731
+    return PrefillWorkload(cfg=cfg, prefix_lens=prefix, chunk_lens=chunk, ctx=ctx,
+                           cu_seqlens_q=cu, tables=tables, prefix_slots=np.concatenate(ps),
+                           prefix_k=cat(pk, (0, hkv, d)), prefix_v=cat(pv, (0, hkv, d)),
+                           chunk_slots=np.concatenate(cs), chunk_k=cat(ck, (0, hkv, d)),
+                           chunk_v=cat(cv, (0, hkv, d)), q=q)

@@ -687,3 +687,101 @@ def test_beam_search_workload_full_size():
     w = S.make_beam_workload("beam_bf16")
     run_beam(w, decode_steps=(len(w.steps) - 1,),
              modes=(w.cfg.partition_size, -1, pa.PA_PARTITION_BALANCED, 0))
+
+
+# --------------------------------------------------------------------------
+# paged prefill
+# --------------------------------------------------------------------------
+def gpu_prefill(q, kd, vd, tab, cu, ctx, scale, max_q_len=None):
+    qd = H.to_dev(q)
+    out = torch.empty_like(qd)
+    cu = np.asarray(cu, dtype=np.int32)
+    mq = int(np.diff(cu).max()) if max_q_len is None else int(max_q_len)
+    pa.pa_prefill(out, qd, kd, vd, H.to_dev(np.asarray(tab, dtype=np.int32)), H.to_dev(cu),
+                  H.to_dev(np.asarray(ctx, dtype=np.int32)), int(np.max(ctx)), mq, scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def prefill_gpu_case(rng, chunks, prefixes, hq, hkv, bs, nb_extra=5):
+    d = 128
+    ctxs = [p + c for p, c in zip(prefixes, chunks)]
+    q = S._normal(rng, (sum(chunks), hq, d), "bf16")
+    kl = [S._normal(rng, (n, hkv, d), "bf16") for n in ctxs]
+    vl = [S._normal(rng, (n, hkv, d), "bf16") for n in ctxs]
+    nb = sum((n + bs - 1) // bs for n in ctxs) + nb_extra
+    kc, vc, tab = H.paginate(kl, vl, bs, nb, rng, "bf16")
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    return q, cu, np.array(ctxs, dtype=np.int32), kc, vc, tab
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("bs", [16, 64])
+def test_prefill_matches_oracle(G, bs):
+    """Chunks of 0, 1, a few and many rows, over empty, short and long
+    prefixes, lengths off every tile and wavefront boundary; unused slots NaN."""
+    rng = np.random.default_rng(100 * G + bs)
+    chunks = [1, 0, 7, 40, 33, 100, 5]
+    prefixes = [0, 12, 0, 1, 250, 77, 600]
+    hkv = 2
+    q, cu, ctx, kc, vc, tab = prefill_gpu_case(rng, chunks, prefixes, hkv * G, hkv, bs)
+    ref = pao.prefill_concat(q, kc, vc, tab, cu, ctx, 0.09)
+    got = gpu_prefill(q, H.to_dev(kc), H.to_dev(vc), tab, cu, ctx, 0.09)
+    H.assert_close_to_oracle(got, ref, "bf16", f"prefill G {G} bs {bs}")
+
+
+def test_prefill_of_one_row_equals_decode():
+    """A chunk of one row is the decode of that query (same tile step)."""
+    rng = np.random.default_rng(3)
+    chunks, prefixes = [1, 1, 1, 1], [0, 15, 300, 1024]
+    q, cu, ctx, kc, vc, tab = prefill_gpu_case(rng, chunks, prefixes, 32, 8, 16)
+    kd, vd = H.to_dev(kc), H.to_dev(vc)
+    a = gpu_prefill(q, kd, vd, tab, cu, ctx, 0.1)
+    b = H.gpu_decode(q, kd, vd, tab, ctx, 0.1, None, 0, MFMA)
+    ref = pao.decode_concat(q, kc, vc, tab, ctx, 0.1)
+    H.assert_close_to_oracle(a, ref, "bf16", "prefill of one row")
+    np.testing.assert_array_equal(a, b)
+
+
+def test_prefill_whole_prompt_then_decode():
+    """Demo 1's order: prefill a whole prompt (chunk = sequence), then decode
+    the next token over the same pool; both match the oracle."""
+    rng = np.random.default_rng(4)
+    n, hq, hkv, d, bs = 300, 16, 4, 128, 16
+    kl = [S._normal(rng, (n + 1, hkv, d), "bf16")]
+    vl = [S._normal(rng, (n + 1, hkv, d), "bf16")]
+    kc, vc, tab = H.paginate(kl, vl, bs, 40, rng, "bf16")
+    q = S._normal(rng, (n, hq, d), "bf16")
+    cu = np.array([0, n], dtype=np.int32)
+    kd, vd = H.to_dev(kc), H.to_dev(vc)
+    ref = pao.prefill_concat(q, kc, vc, tab, cu, np.array([n]), 0.088)
+    got = gpu_prefill(q, kd, vd, tab, cu, np.array([n]), 0.088)
+    H.assert_close_to_oracle(got, ref, "bf16", "whole-prompt prefill")
+    qn = S._normal(rng, (1, hq, d), "bf16")
+    ref2 = pao.decode_concat(qn, kc, vc, tab, np.array([n + 1]), 0.088)
+    got2 = H.gpu_decode(qn, kd, vd, tab, np.array([n + 1]), 0.088, None, -1)
+    H.assert_close_to_oracle(got2, ref2, "bf16", "decode after prefill")
+
+
+def test_prefill_workload_full_size():
+    """16 sequences, 512-row chunks over prefixes up to 1536: the chunk's K/V
+    go in through pa_reshape_and_cache, then pa_prefill; sampled sequences
+    match the oracle, the pool matches bit for bit."""
+    w = S.make_prefill_workload("prefill_bf16")
+    c = w.cfg
+    cfg = S.Config(name=c.name, seed=c.seed, num_seqs=c.num_seqs, num_q_heads=c.num_q_heads,
+                   num_kv_heads=c.num_kv_heads, head_dim=c.head_dim, block_size=c.block_size,
+                   num_blocks=c.num_blocks, max_blocks_per_seq=c.max_blocks_per_seq,
+                   dtype=c.dtype, scale=c.scale, description="")
+    kh, vh = H.empty_pool(cfg)
+    kd, vd = H.dev_empty_pool(cfg)
+    for k, v, s in ((w.prefix_k, w.prefix_v, w.prefix_slots), (w.chunk_k, w.chunk_v, w.chunk_slots)):
+        pao.slot_write(kh, vh, k, v, s, c.block_size)
+        H.dev_write(kd, vd, k, v, s)
+    np.testing.assert_array_equal(H.to_host(kd), kh)
+    got = gpu_prefill(w.q, kd, vd, w.tables, w.cu_seqlens_q, w.ctx, c.scale)
+    for b in (0, int(np.argmax(w.ctx)), int(np.argmin(w.ctx))):
+        q0, q1 = w.cu_seqlens_q[b], w.cu_seqlens_q[b + 1]
+        ref = pao.prefill_concat(w.q[q0:q1], kh, vh, w.tables[b:b + 1],
+                                 np.array([0, q1 - q0]), w.ctx[b:b + 1], c.scale)
+        H.assert_close_to_oracle(got[q0:q1], ref, "bf16", f"prefill workload seq {b}")
