@@ -7,10 +7,11 @@ one HIP stream, with every input already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
-NAME is one of the decode workloads (default gqa_bf16) or a beam-search
+NAME is one of the decode workloads (default gqa_bf16), a beam-search
 workload (beam_bf16, beam_tiny_bf16), whose measured step is its last one:
 that step's copy-on-write block copies (pa_copy_blocks), its slot write and
-the decode of every beam.
+the decode of every beam, or the chunked-prefill workload (prefill_bf16):
+the chunk's slot write plus pa_prefill, priced against the matrix-core peak.
 
 Prints ONE JSON line.  `value` is the achieved KV-read bandwidth of the whole
 step (logical KV bytes the step's queries read / step time, in GB/s);
@@ -40,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved KV-read GB/s (% HBM peak) and tokens/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 DEFAULT_CONFIG = "gqa_bf16"
 KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_shared.hip", "pa_decode_vector.hip",
                   "pa_reduce.hip", "pa_cache_write.hip", "pa_api.cpp", "pa_internal.h",
@@ -202,6 +204,80 @@ def cpu_baseline(w, target_seconds):
                               "sample": f"first {n1} sequences, {t1:.3f} s"}}
 
 
+def bench_prefill(args, torch, pa, S, dev):
+    """A prefill step: the chunk's slot write plus causal prefill of every
+    chunk row.  The prefill kernel is priced against the bf16 matrix-core
+    peak (its flops: 4 d Hq per (query row, visible key))."""
+    w = S.make_prefill_workload(args.config)
+    c = w.cfg
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+    k_cache = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    v_cache = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    pa.pa_reshape_and_cache(dev_t(w.prefix_k), dev_t(w.prefix_v), k_cache, v_cache,
+                            dev_t(w.prefix_slots))
+    ck, cv, cs = dev_t(w.chunk_k), dev_t(w.chunk_v), dev_t(w.chunk_slots)
+    q, tables, cu, ctx = dev_t(w.q), dev_t(w.tables), dev_t(w.cu_seqlens_q), dev_t(w.ctx)
+    out = torch.empty_like(q)
+    max_ctx, max_q = int(w.ctx.max()), int(w.chunk_lens.max())
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        pa.pa_reshape_and_cache(ck, cv, k_cache, v_cache, cs, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        pa.pa_prefill(out, q, k_cache, v_cache, tables, cu, ctx, max_ctx, max_q, c.scale,
+                      stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    t_write = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    t_pf = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    ms_step = wall / args.steps * 1e3
+    flops = w.flops()
+    kv = w.kv_bytes()
+    tflops = flops / (t_pf * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": round(kv / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": c.name, "description": c.description, "batch": c.num_seqs,
+                   "total_q": int(w.cu_seqlens_q[-1]), "sum_context": int(w.ctx.sum()),
+                   "num_q_heads": c.num_q_heads, "num_kv_heads": c.num_kv_heads,
+                   "head_dim": c.head_dim, "block_size": c.block_size,
+                   "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(int(w.cu_seqlens_q[-1]) / (ms_step * 1e-3), 1),
+        "kernels_ms": {"reshape_and_cache": round(t_write, 5), "prefill": round(t_pf, 5)},
+        "flops": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_mfma_kernel"},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -222,6 +298,8 @@ def main():
     torch.cuda.set_device(dev)
     algo = {"auto": pa.PA_ALGO_AUTO, "vector": pa.PA_ALGO_VECTOR, "mfma": pa.PA_ALGO_MFMA}[args.algo]
 
+    if args.config in S.PREFILL_CONFIGS:
+        return bench_prefill(args, torch, pa, S, dev)
     log(f"building workload {args.config}")
     w = BeamLastStep(S.make_beam_workload(args.config)) if args.config in S.BEAM_CONFIGS \
         else S.make_workload(args.config)

@@ -108,6 +108,12 @@ __global__ __launch_bounds__(kWave) void plan_shared_kernel(const SharedParams p
 #ifndef PA_SHARED_WAVES_PER_EU
 #define PA_SHARED_WAVES_PER_EU 2
 #endif
+// Items whose loads are in flight while one is computed.
+#ifndef PA_SHARED_DEPTH
+#define PA_SHARED_DEPTH 1
+#endif
+constexpr int kSD = PA_SHARED_DEPTH;
+constexpr int kSB = kSD + 1;
 
 template <int NPK, int NCG>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PA_SHARED_WAVES_PER_EU)))
@@ -151,8 +157,10 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
     const int C = (total + W - 1) / W;
 
     // this lane's columns, one per column group of 16: column
-    // cg * 16 + row16 is head hj of member im of the pack
-    int im[NCG], hj[NCG];
+    // cg * 16 + row16 is head hj of member im of the pack; group_members[cg]:
+    // the members with a column in group cg (an item none of them references
+    // leaves the group untouched and is skipped for it)
+    int im[NCG], hj[NCG], group_members[NCG];
     bool col_real[NCG];
 #pragma unroll
     for (int cg = 0; cg < NCG; cg++) {
@@ -160,6 +168,8 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
         im[cg] = col / G;
         hj[cg] = col - im[cg] * G;
         col_real[cg] = im[cg] < NPK;
+        const int lo = (cg * 16) / G, hi = min(NPK - 1, (cg * 16 + 15) / G);
+        group_members[cg] = lo > hi ? 0 : ((1 << (hi + 1)) - 1) & ~((1 << lo) - 1);
     }
 
     const char *kbase = (const char *)p.k_cache;
@@ -208,34 +218,40 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
             acc_init(a[cg]);
         }
 
-        // items q_begin .. q_end-1; the loads of item q+1 are issued before
-        // item q is computed, and the record of item q+2 is read meanwhile
+        // items q_begin .. q_end-1; the loads of items q+1 .. q+kSD are in
+        // flight while item q is computed, and the record of the next item to
+        // issue is read one item ahead
         const int4 *list = ws_items + (size_t)k * NPK * p.max_tiles;
         auto issue = [&](const int4 &it, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
             const size_t off = ((((size_t)it.x * p.num_kv_heads + g) << p.log2_block) +
                                 ((it.y * kTile) & bs_mask)) * (size_t)kRowBytes;
             load_tile_rows(kbase, vbase, off, it.z & 0xff, ln, kr, vr);
         };
-        u32x4 kr[2][4], vr[2][4];
-        int4 rec[2];
-        rec[0] = list[q_begin];
-        int4 ahead = list[min(q_begin + 1, q_end - 1)];
-        issue(rec[0], kr[0], vr[0]);
-        for (int q0 = q_begin; q0 < q_end; q0 += 2) {
+        const int4 none = make_int4(0, 0, 0, 0);
+        u32x4 kr[kSB][4], vr[kSB][4];
+        int4 rec[kSB];
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
+        for (int j = 0; j < kSD; j++) {
+            rec[j] = q_begin + j < q_end ? list[q_begin + j] : none;
+            issue(rec[j], kr[j], vr[j]);
+        }
+        int4 ahead = list[min(q_begin + kSD, q_end - 1)];
+        for (int q0 = q_begin; q0 < q_end; q0 += kSB) {
+#pragma unroll
+            for (int j = 0; j < kSB; j++) {
                 const int q = q0 + j;
                 if (q >= q_end) break;
-                const int4 nxt = q + 1 < q_end ? ahead : make_int4(0, 0, 0, 0);
-                ahead = list[min(q + 2, q_end - 1)];
-                rec[(j + 1) & 1] = nxt;
-                issue(nxt, kr[(j + 1) & 1], vr[(j + 1) & 1]);
+                const int jn = (j + kSD) % kSB;
+                rec[jn] = q + kSD < q_end ? ahead : none;
+                ahead = list[min(q + kSD + 1, q_end - 1)];
+                issue(rec[jn], kr[jn], vr[jn]);
                 __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the wait
                 const int4 it = rec[j];
                 if ((it.z & 0xff) > 0) {
                     const int mask = it.z >> 8;
 #pragma unroll
                     for (int cg = 0; cg < NCG; cg++) {
+                        if ((mask & group_members[cg]) == 0) continue;   // none of its columns
                         const bool in_mask = col_ok[cg] && ((mask >> im[cg]) & 1);
                         const int nv = in_mask ? n_col[cg] - it.y * kTile : 0;
                         tile_update<true>(kr[j], vr[j], qv[cg], nv, p.scale_log2, a[cg], ln);
