@@ -334,7 +334,7 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
     p.log2_block = ilog2(block_size);
     p.max_blocks_per_seq = max_blocks_per_seq;
     p.max_context_len = max_context_len;
-    const int rows_per_wave = 32 / p.group;
+    const int rows_per_wave = pa::kPrefillColumns / p.group;
     p.units_per_seq = (max_q_len + rows_per_wave - 1) / rows_per_wave;
     p.scale_log2 = scale * 1.4426950408889634f;
     if ((int64_t)num_seqs * num_kv_heads * p.units_per_seq > 0x7fffffff) return PA_ERR_SHAPE;

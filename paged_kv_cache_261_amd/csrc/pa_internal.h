@@ -105,7 +105,7 @@ struct PrefillParams {
     int log2_block;
     int max_blocks_per_seq;
     int max_context_len;
-    int units_per_seq;         // ceil(max_q_len / rows per wavefront)
+    int units_per_seq;         // wavefronts per (sequence, KV head): ceil(max_q_len / rows per wavefront)
     float scale_log2;
 };
 
@@ -154,6 +154,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // Launchers: validate nothing (pa_api.cpp does), enqueue, return hipError_t.
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
+// query-head columns one prefill wavefront serves (two 16-column groups)
+constexpr int kPrefillColumns = 32;
 hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int num_pairs,
                               int num_blocks, int64_t block_bytes, hipStream_t stream);
 hipError_t launch_cache_write(const void *k, const void *v, void *k_cache, void *v_cache,

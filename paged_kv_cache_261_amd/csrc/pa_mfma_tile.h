@@ -145,8 +145,15 @@ __device__ __forceinline__ void tile_update(const u32x4 (&kr)[4], const u32x4 (&
     for (int i = 0; i < 4; i++) pr[i] = fast_exp2(s[i] - shift);
     a.lsum = a.lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     a.m = m_new;
+    // once the running max settles, alpha is 1 for every column and the
+    // rescale would multiply by one: skip it (same bits, fewer VALU ops)
+#ifndef PA_NO_RESCALE_SKIP
+    if (__ballot(alpha != 1.f) != 0)
+#endif
+    {
 #pragma unroll
-    for (int nn = 0; nn < 8; nn++) a.o[nn] *= alpha;
+        for (int nn = 0; nn < 8; nn++) a.o[nn] *= alpha;
+    }
     const s16x4 pb = __builtin_bit_cast(
         s16x4, (uint2){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
 #pragma unroll

@@ -21,7 +21,7 @@
 
 namespace pa {
 
-constexpr int kPrefillCols = 32;
+constexpr int kPrefillCols = kPrefillColumns;
 
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ tables,
