@@ -15,7 +15,7 @@
 // (demo 3 observations).
 //
 // Three kernels:
-//  1. plan_shared_kernel, one wavefront per pack: lists the pack's items.
+//  1. plan_shared_kernel, one workgroup per pack: lists the pack's items.
 //     At tile index t, member i owns an item when it is the first member (in
 //     order) that reaches t with its block id; the item is (block id, t, the
 //     members with that id, the most rows any of them sees).  Items are
@@ -37,11 +37,17 @@ namespace pa {
 // 1. Plan: the item list of each pack.
 // ---------------------------------------------------------------------------
 // Item record (16 bytes): block id (0 when out of range, with rows 0), tile
-// index, rows | member mask << 8, unused.
+// index, rows | member mask << 8, unused.  One workgroup per pack, one
+// thread per tile index (in chunks of blockDim.x): each thread counts its
+// tile's items, a workgroup-wide prefix places them.
+constexpr int kPlanMaxThreads = 1024;
+
 template <int NPK>
-__global__ __launch_bounds__(kWave) void plan_shared_kernel(const SharedParams p) {
+__global__ __launch_bounds__(kPlanMaxThreads) void plan_shared_kernel(const SharedParams p) {
+    __shared__ int wave_sum[kPlanMaxThreads / kWave];
     const int k = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    const int nw = blockDim.x / kWave;
     int n[NPK];
     int maxT = 0;
 #pragma unroll
@@ -52,8 +58,8 @@ __global__ __launch_bounds__(kWave) void plan_shared_kernel(const SharedParams p
     }
     int4 *items = (int4 *)p.ws_items + (size_t)k * NPK * p.max_tiles;
     int running = 0;
-    for (int t0 = 0; t0 < maxT; t0 += kWave) {
-        const int t = t0 + lane;
+    for (int t0 = 0; t0 < maxT; t0 += blockDim.x) {
+        const int t = t0 + tid;
         int id[NPK];
         bool v[NPK];
 #pragma unroll
@@ -77,8 +83,16 @@ __global__ __launch_bounds__(kWave) void plan_shared_kernel(const SharedParams p
             const int y = __shfl_up(incl, off);
             if (lane >= off) incl += y;
         }
-        // this tile index's items go to [running + incl - cost, running + incl)
-        int q = running + incl - cost;
+        if (lane == kWave - 1) wave_sum[wv] = incl;
+        __syncthreads();
+        int before = 0, chunk = 0;
+        for (int j = 0; j < nw; j++) {
+            const int sj = wave_sum[j];
+            before += j < wv ? sj : 0;
+            chunk += sj;
+        }
+        // this tile index's items go to [running + before + incl - cost, ... + cost)
+        int q = running + before + incl - cost;
 #pragma unroll
         for (int i = 0; i < NPK; i++) {
             bool dup = false;
@@ -97,16 +111,17 @@ __global__ __launch_bounds__(kWave) void plan_shared_kernel(const SharedParams p
                 items[q++] = make_int4(ok ? id[i] : 0, t, rows | (mask << 8), 0);
             }
         }
-        running += __shfl(incl, kWave - 1);
+        running += chunk;
+        __syncthreads();                 // wave_sum is rewritten by the next chunk
     }
-    if (lane == 0) p.ws_cost[k] = running;
+    if (tid == 0) p.ws_cost[k] = running;
 }
 
 // ---------------------------------------------------------------------------
 // 2. Decode over packs.
 // ---------------------------------------------------------------------------
 #ifndef PA_SHARED_WAVES_PER_EU
-#define PA_SHARED_WAVES_PER_EU 2
+#define PA_SHARED_WAVES_PER_EU 1
 #endif
 // Items whose loads are in flight while one is computed.
 #ifndef PA_SHARED_DEPTH
@@ -133,10 +148,6 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
     const int w = xcd_remap(blockIdx.x, W);
     const int G = p.group;
     const int NPACK = p.num_packs;
-    if (lane == 0) {
-        ws_dir[2 * w] = -1;
-        ws_dir[2 * w + 1] = -1;
-    }
 
     // item-count prefix over packs: lane i owns packs [i K, i K + K)
     const int K = (NPACK + kWave - 1) / kWave;
@@ -177,7 +188,33 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
     const int bs_mask = (1 << p.log2_block) - 1;
     const int x1 = min(w * C + C, total);
     int x = w * C;
+
+    // A finished pack's state is written out late: a store counts in the
+    // same in-order counter as the loads, so a store issued between two
+    // tile loads holds up the wait for the later one.  The state of the
+    // wave's first pack waits in `pend` until the next pack's first loads
+    // are in flight, or, if that pack is the wave's last, until the end.
+    // Partial states go to the wave's two slots (only its first and last
+    // packs can be partial); dir[] records which unit each slot holds.
+    Acc pend[NCG];
+    bool have_pend = false, pend_whole = false;
+    int pend_g = 0, pend_k = 0, pend_slot = 0;
     int slot = 0;
+    int dir0 = -1, dir1 = -1;
+    auto emit = [&](const Acc (&st)[NCG], bool whole, int g, int k, int sl) {
+#pragma unroll
+        for (int cg = 0; cg < NCG; cg++) {
+            if (whole) {
+                const int b = k * NPK + (col_real[cg] ? im[cg] : 0);
+                if (col_real[cg] && b < p.num_seqs)
+                    store_row((char *)out + ((size_t)b * p.num_q_heads + g * G + hj[cg]) * kD * 2,
+                              st[cg], ln);
+            } else {
+                const size_t prow = ((size_t)w * 2 + sl) * kMaxCols + cg * 16 + ln.row16;
+                store_partial(ws_m + prow, ws_l + prow, ws_acc + prow * kD, st[cg], ln);
+            }
+        }
+    };
     while (x < x1) {
         const int g = x / TT;
         const int r = x - g * TT;
@@ -186,15 +223,21 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
         const int jl = __builtin_ctzll(own);
         int base = __builtin_amdgcn_readfirstlane(__shfl(excl, jl));
         int k = jl * K;
-        int Uk = __builtin_amdgcn_readfirstlane(ws_cost[k]);
-        while (r >= base + Uk) {
-            base += Uk;
-            k++;
+        int Uk;
+        if (K == 1) {
+            Uk = __builtin_amdgcn_readfirstlane(__shfl(local, jl));
+        } else {
             Uk = __builtin_amdgcn_readfirstlane(ws_cost[k]);
+            while (r >= base + Uk) {
+                base += Uk;
+                k++;
+                Uk = __builtin_amdgcn_readfirstlane(ws_cost[k]);
+            }
         }
         const int q_begin = r - base;                  // items [q_begin, q_end) of pack k
         const int q_end = min(Uk, q_begin + (x1 - x));
         x += q_end - q_begin;
+        const bool last_pack = x >= x1;
 
         // this lane's columns within the pack
         int b_col[NCG], n_col[NCG];
@@ -219,9 +262,34 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
         }
 
         // items q_begin .. q_end-1; the loads of items q+1 .. q+kSD are in
-        // flight while item q is computed, and the record of the next item to
-        // issue is read one item ahead
+        // flight while item q is computed.  Item records are held in two
+        // VGPR windows of 64 (lane i: record base + i) and read out with lane
+        // reads; the window just left is reloaded with the one after next,
+        // a whole window ahead of its use, so no memory round trip sits
+        // between computing one item and issuing the next.  The two windows
+        // alternate instead of being copied: a copy of a freshly loaded
+        // register would wait for its load.
         const int4 *list = ws_items + (size_t)k * NPK * p.max_tiles;
+        const int last = q_end - 1;
+        int wb = q_begin;                            // first record of the current window
+        bool in_b = false;                           // current window: wB (else wA)
+        const u32x4 *rlist = (const u32x4 *)list;
+        const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)list, (short)0, q_end * 16, kRsrcWord3);
+        u32x4 wA = rlist[min(wb + lane, last)];
+        u32x4 wB = rlist[min(wb + kWave + lane, last)];
+        auto record = [&](int q) -> int4 {           // q in [wb, wb + 64), uniform
+            const int i = q - wb;
+            int4 r;
+            if (in_b) {
+                r = make_int4(__builtin_amdgcn_readlane(wB[0], i), __builtin_amdgcn_readlane(wB[1], i),
+                              __builtin_amdgcn_readlane(wB[2], i), 0);
+            } else {
+                r = make_int4(__builtin_amdgcn_readlane(wA[0], i), __builtin_amdgcn_readlane(wA[1], i),
+                              __builtin_amdgcn_readlane(wA[2], i), 0);
+            }
+            return r;
+        };
         auto issue = [&](const int4 &it, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
             const size_t off = ((((size_t)it.x * p.num_kv_heads + g) << p.log2_block) +
                                 ((it.y * kTile) & bs_mask)) * (size_t)kRowBytes;
@@ -232,18 +300,34 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
         int4 rec[kSB];
 #pragma unroll
         for (int j = 0; j < kSD; j++) {
-            rec[j] = q_begin + j < q_end ? list[q_begin + j] : none;
+            rec[j] = q_begin + j < q_end ? record(q_begin + j) : none;
             issue(rec[j], kr[j], vr[j]);
         }
-        int4 ahead = list[min(q_begin + kSD, q_end - 1)];
+        if (have_pend && !last_pack) {
+            emit(pend, pend_whole, pend_g, pend_k, pend_slot);
+            have_pend = false;
+        }
         for (int q0 = q_begin; q0 < q_end; q0 += kSB) {
 #pragma unroll
             for (int j = 0; j < kSB; j++) {
                 const int q = q0 + j;
                 if (q >= q_end) break;
                 const int jn = (j + kSD) % kSB;
-                rec[jn] = q + kSD < q_end ? ahead : none;
-                ahead = list[min(q + kSD + 1, q_end - 1)];
+                if (q + kSD == wb + kWave) {           // into the next window
+                    // the two branches load through different instructions
+                    // (a pointer read, a buffer read) so that the compiler
+                    // keeps each load in its branch, writing straight into
+                    // the window it refills
+                    const int idx = min(wb + 2 * kWave + lane, last);
+                    if (in_b)
+                        wB = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           lrs, idx * 16, 0, 0));
+                    else
+                        wA = rlist[idx];
+                    wb += kWave;
+                    in_b = !in_b;
+                }
+                rec[jn] = q + kSD < q_end ? record(q + kSD) : none;
                 issue(rec[jn], kr[jn], vr[jn]);
                 __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the wait
                 const int4 it = rec[j];
@@ -262,22 +346,31 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
 
         const bool whole = q_begin == 0 && q_end == Uk;
 #pragma unroll
-        for (int cg = 0; cg < NCG; cg++) {
-            acc_finish(a[cg]);
-            if (whole) {
-                if (col_ok[cg])
-                    store_row((char *)out + ((size_t)b_col[cg] * p.num_q_heads + g * G + hj[cg]) *
-                                                kD * 2,
-                              a[cg], ln);
-            } else {
-                const size_t prow = ((size_t)w * 2 + slot) * kMaxCols + cg * 16 + ln.row16;
-                store_partial(ws_m + prow, ws_l + prow, ws_acc + prow * kD, a[cg], ln);
-            }
-        }
+        for (int cg = 0; cg < NCG; cg++) acc_finish(a[cg]);
+        int sl = 0;
         if (!whole) {
-            if (lane == 0) ws_dir[2 * w + slot] = g * NPACK + k;
+            sl = slot;
+            if (slot == 0) dir0 = g * NPACK + k; else dir1 = g * NPACK + k;
             slot = 1;
         }
+        if (have_pend) {                 // this is the wave's last pack
+            emit(pend, pend_whole, pend_g, pend_k, pend_slot);
+            have_pend = false;
+            emit(a, whole, g, k, sl);
+        } else {
+#pragma unroll
+            for (int cg = 0; cg < NCG; cg++) pend[cg] = a[cg];
+            have_pend = true;
+            pend_whole = whole;
+            pend_g = g;
+            pend_k = k;
+            pend_slot = sl;
+        }
+    }
+    if (have_pend) emit(pend, pend_whole, pend_g, pend_k, pend_slot);
+    if (lane == 0) {
+        ws_dir[2 * w] = dir0;
+        ws_dir[2 * w + 1] = dir1;
     }
 }
 
@@ -393,7 +486,11 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
 template <int NPK, int NCG>
 static hipError_t launch_shared_t(const SharedParams &p, int phase, hipStream_t stream) {
     if (phase & 1) {
-        hipLaunchKernelGGL(plan_shared_kernel<NPK>, dim3(p.num_packs), dim3(kWave), 0, stream, p);
+        // one thread per tile index, up to kPlanMaxThreads (then chunks)
+        const int plan_threads =
+            std::min(kPlanMaxThreads, std::max(kWave, (p.max_tiles + kWave - 1) / kWave * kWave));
+        hipLaunchKernelGGL(plan_shared_kernel<NPK>, dim3(p.num_packs), dim3(plan_threads), 0,
+                           stream, p);
         hipLaunchKernelGGL((decode_shared_kernel<NPK, NCG>), dim3(p.num_waves), dim3(kWave), 0,
                            stream, p, p.context_lens, p.out, p.ws_m, p.ws_l, p.ws_acc, p.ws_dir,
                            p.ws_cost, (const int4 *)p.ws_items);

@@ -86,19 +86,23 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
                             ((t * kTile) & bs_mask)) * (size_t)kRowBytes;
         load_tile_rows(kbase, vbase, off, rows, ln, kr, vr);
     };
+    // phys[j]: block id of the tile in buffer j (kept, not re-read, so no
+    // table read sits between a tile's compute and the next load)
     u32x4 kr[2][4], vr[2][4];
-    int phys_next = phys_of(0);
-    issue(0, phys_next, kr[0], vr[0]);
-    phys_next = phys_of(1);
+    int phys[2];
+    phys[0] = phys_of(0);
+    issue(0, phys[0], kr[0], vr[0]);
+    int phys_next = phys_of(1);
     for (int t0 = 0; t0 < ntiles; t0 += 2) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int t = t0 + j;
             if (t >= ntiles) break;
+            phys[j ^ 1] = phys_next;
             issue(t + 1, phys_next, kr[j ^ 1], vr[j ^ 1]);
             phys_next = phys_of(t + 2);
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the wait
-            if ((unsigned)table[(t * kTile) >> log2bs] < (unsigned)p.num_blocks) {
+            if ((unsigned)phys[j] < (unsigned)p.num_blocks) {
 #pragma unroll
                 for (int cg = 0; cg < 2; cg++)
                     tile_update<true>(kr[j], vr[j], qv[cg], ncol[cg] - t * kTile, p.scale_log2,
