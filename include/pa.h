@@ -78,7 +78,7 @@ enum {
 /* Special partition_size values for pa_decode / pa_decode_partitions /
  * pa_decode_reduce / pa_decode_workspace_size. */
 #define PA_PARTITION_AUTO (-1)      /* the library chooses                     */
-#define PA_PARTITION_BALANCED (-2)  /* work-balanced split (matrix-core path)  */
+#define PA_PARTITION_BALANCED (-2)  /* work-balanced split                     */
 #define PA_PARTITION_SHARED (-3)    /* balanced split that reads blocks shared
                                        by neighbouring sequences once
                                        (matrix-core path)                      */
@@ -170,10 +170,14 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
  * partition_size == PA_PARTITION_AUTO for these sizes and PA_ALGO_AUTO:
  * 0 (single pass, no workspace), PA_PARTITION_BALANCED, or a multiple of
  * block_size.  A pure function of its arguments.  Where the vector kernel
- * runs (every shape the matrix-core kernels do not take, or PA_ALGO_VECTOR)
- * the partition is the power of two from 64 to 512 tokens (at least
- * block_size) that gives about 8192 wavefronts for contexts of
- * max_context_len, or single pass for small problems.
+ * runs (every shape the matrix-core kernels do not take, or PA_ALGO_VECTOR):
+ * single pass for small problems (max_context_len * num_seqs *
+ * num_kv_heads <= 65536, or a context that fits one partition below);
+ * otherwise PA_PARTITION_BALANCED when block_size >= 16 and the head's
+ * 16-token tile covers whole 64-lane load passes (every head_dim for
+ * float32, head_dim >= 32 for bfloat16), else the power of two from 64 to
+ * 512 tokens (at least block_size) that gives about 8192 wavefronts for
+ * contexts of max_context_len.
  */
 int pa_decode_auto_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_context_len, int dtype);
@@ -210,11 +214,15 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
  *   partition_size   0: single pass, one work unit per (sequence, KV head);
  *                 PA_PARTITION_AUTO: the library chooses
  *                 (pa_decode_auto_partition);
- *                 PA_PARTITION_BALANCED: work-balanced split (matrix-core
- *                 path only): the 16-token tiles of every (KV head,
- *                 sequence) are laid end to end and a fixed number of
- *                 wavefronts take equal contiguous shares; pieces of a
- *                 context cut between wavefronts are merged by log-sum-exp;
+ *                 PA_PARTITION_BALANCED: work-balanced split: the 16-token
+ *                 tiles of every (KV head, sequence) are laid end to end
+ *                 and a fixed number of wavefronts take equal contiguous
+ *                 shares; pieces of a context cut between wavefronts are
+ *                 merged by log-sum-exp.  Needs block_size >= 16; runs on
+ *                 the matrix cores where they apply (unless algo is
+ *                 PA_ALGO_VECTOR), else on the vector ALUs, which take
+ *                 float32 with any head_dim and bfloat16 with head_dim >= 32
+ *                 (PA_ERR_ALGO otherwise);
  *                 PA_PARTITION_SHARED: like PA_PARTITION_BALANCED, but
  *                 consecutive sequences are taken in packs (8 when the
  *                 group size is at most 4, 4 up to 8, 2 up to 16) whose

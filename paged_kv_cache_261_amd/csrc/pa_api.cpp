@@ -58,6 +58,23 @@ bool balanced_applies(int dtype, int head_dim, int block_size, int num_q_heads,
            num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads <= 16;
 }
 
+// The work-balanced split on the vector ALUs (any dtype; block_size >= 16;
+// head dims whose 16-token tile covers whole 64-lane load passes).
+bool vector_balanced_applies(int dtype, int head_dim, int block_size, int num_q_heads,
+                             int num_kv_heads) {
+    return head_dim_ok(head_dim) && dtype_ok(dtype) && block_size_ok(block_size) &&
+           pa::vector_balanced_supported(head_dim, dtype == PA_BF16 ? 1 : 0, block_size) &&
+           num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+           num_q_heads / num_kv_heads <= 16;
+}
+
+// Either balanced split applies.
+bool any_balanced_applies(int dtype, int head_dim, int block_size, int num_q_heads,
+                          int num_kv_heads) {
+    return balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads) ||
+           vector_balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads);
+}
+
 // Partition size for the vector kernel (one wavefront per (sequence, KV
 // head, partition)): small enough that about kVectorWaves wavefronts have
 // work when every context is max_context_len long -- the kernel hides
@@ -82,7 +99,8 @@ int resolve_partition(int partition_size, int num_seqs, int num_q_heads, int num
     if (partition_size != PA_PARTITION_AUTO) return partition_size;
     const int p = pa_decode_auto_partition(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                            block_size, max_context_len, dtype);
-    if (p == PA_PARTITION_BALANCED && algo == PA_ALGO_VECTOR)
+    if (p == PA_PARTITION_BALANCED && algo == PA_ALGO_VECTOR &&
+        !vector_balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads))
         return vector_partition(num_seqs, num_kv_heads, block_size, max_context_len);
     return p;
 }
@@ -168,21 +186,40 @@ bool mfma_applies(const DecodeArgs &a) {
            a.num_q_heads / a.num_kv_heads <= 16;
 }
 
+bool vector_balanced_applies(const DecodeArgs &a) {
+    return vector_balanced_applies(a.dtype, a.head_dim, a.block_size, a.num_q_heads,
+                                   a.num_kv_heads);
+}
+
+// Which kernel runs the work-balanced split: the matrix cores unless the
+// caller asks for the vector ALUs (or the shape needs them).  -1: neither
+// applies.
+int balanced_kernel(const DecodeArgs &a) {
+    if (a.algo != PA_ALGO_VECTOR && mfma_applies(a)) return PA_ALGO_MFMA;
+    if (a.algo != PA_ALGO_MFMA && vector_balanced_applies(a)) return PA_ALGO_VECTOR;
+    return -1;
+}
+
 // Phase 1 (or the whole decode when num_partitions == 1).
 int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *ws_m,
                  float *ws_l, float *ws_acc, hipStream_t stream) {
     const bool balanced = partition == PA_PARTITION_BALANCED;
     bool use_mfma;
-    if (a.algo == PA_ALGO_MFMA || balanced) {
-        if (!mfma_applies(a) || a.algo == PA_ALGO_VECTOR) return PA_ERR_ALGO;
+    if (balanced) {
+        const int k = balanced_kernel(a);
+        if (k < 0) return PA_ERR_ALGO;
+        use_mfma = k == PA_ALGO_MFMA;
+    } else if (a.algo == PA_ALGO_MFMA) {
+        if (!mfma_applies(a)) return PA_ERR_ALGO;
         use_mfma = true;
     } else {
         use_mfma = a.algo == PA_ALGO_AUTO && mfma_applies(a);
     }
     // Matrix-core path: single pass runs one wavefront per (sequence, KV
-    // head); every split runs the persistent wavefronts.  Vector path: one
-    // wavefront per (sequence, KV head, partition).
-    const bool persistent = use_mfma && num_partitions != 1;
+    // head); every split runs the persistent wavefronts.  Vector path: the
+    // balanced split runs the persistent wavefronts, fixed partitions and
+    // the single pass one wavefront per (sequence, KV head, partition).
+    const bool persistent = (use_mfma && num_partitions != 1) || (!use_mfma && balanced);
     const int64_t units = persistent ? kBalancedWaves
                                      : (int64_t)num_partitions * a.num_kv_heads * a.num_seqs;
     if (units > 0x7fffffff) return PA_ERR_SHAPE;
@@ -210,8 +247,10 @@ int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *
     p.num_units = (int)units;
     p.persistent = persistent ? 1 : 0;
 
-    const hipError_t e = use_mfma ? pa::launch_decode_mfma(p, stream)
-                                  : pa::launch_decode_vector(p, a.head_dim, a.dtype, stream);
+    const hipError_t e =
+        use_mfma ? pa::launch_decode_mfma(p, stream)
+        : balanced ? pa::launch_decode_vector_balanced(p, a.head_dim, a.dtype, stream)
+                   : pa::launch_decode_vector(p, a.head_dim, a.dtype, stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -347,7 +386,10 @@ int pa_decode_auto_partition(int num_seqs, int num_q_heads, int num_kv_heads, in
     if (!block_size_ok(block_size)) return 0;
     if (balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads))
         return PA_PARTITION_BALANCED;
-    return vector_partition(num_seqs, num_kv_heads, block_size, max_context_len);
+    const int p = vector_partition(num_seqs, num_kv_heads, block_size, max_context_len);
+    if (p > 0 && vector_balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads))
+        return PA_PARTITION_BALANCED;
+    return p;
 }
 
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -373,8 +415,11 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
         return best;
     }
     const int partition = partition_size;
-    if (is_split_mode(partition)) {
+    if (partition == PA_PARTITION_SHARED) {
         if (!balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads)) return 0;
+    } else if (partition == PA_PARTITION_BALANCED) {
+        if (!any_balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads))
+            return 0;
     } else if (partition <= 0 || partition % block_size) {
         return 0;
     }
@@ -397,8 +442,10 @@ int pa_decode_partitions(void *out, const void *q, const void *k_cache, const vo
     if (rc != PA_OK) return rc;
     const int partition = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads,
                                             head_dim, block_size, max_context_len, dtype, algo);
-    if (is_split_mode(partition)) {
+    if (partition == PA_PARTITION_SHARED) {
         if (!mfma_applies(a) || algo == PA_ALGO_VECTOR) return PA_ERR_ALGO;
+    } else if (partition == PA_PARTITION_BALANCED) {
+        if (balanced_kernel(a) < 0) return PA_ERR_ALGO;
     } else if (partition <= 0 || partition % block_size) {
         return PA_ERR_SHAPE;
     }
@@ -426,7 +473,8 @@ int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int n
         (partition_size <= 0 && !balanced) || num_q_heads % num_kv_heads)
         return PA_ERR_SHAPE;
     if (!dtype_ok(dtype) || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
-    if (balanced && (head_dim != 128 || dtype != PA_BF16 || num_q_heads / num_kv_heads > 16))
+    if (balanced && num_q_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+    if (partition_size == PA_PARTITION_SHARED && (head_dim != 128 || dtype != PA_BF16))
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
     if (!out || !context_lens) return PA_ERR_NULL;

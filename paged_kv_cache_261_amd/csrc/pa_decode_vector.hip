@@ -228,6 +228,354 @@ __global__ __launch_bounds__(kWave) void decode_vector_kernel(const DecodeParams
     }
 }
 
+// ---------------------------------------------------------------------------
+// Work-balanced split on the vector ALUs (block_size >= 16).
+//
+// W persistent wavefronts split the stream of 16-token tiles (KV head
+// slowest, then sequence, then tile; a sequence of n tokens has ceil(n/16)
+// tiles per KV head) into equal contiguous shares, exactly as the
+// matrix-core balanced split does, so the same merge kernel combines the
+// pieces: a wavefront finishes the units it covers whole in place and
+// leaves its first and last unit, if partial, in its partial slots 0 and 1.
+//
+// A tile of one (block, KV head) is 16 contiguous rows of head_dim values.
+// Lane (r, c) = (lane / LPT, lane % LPT) loads 16-byte chunk c of row
+// i * TPW + r in pass i, through a buffer descriptor that covers only the
+// tile's visible rows (the rest read as zero), so the tile loop has no
+// branches and the loads of the next tiles are in flight while one is
+// computed.  The block-table entry of a tile is
+// read with a scalar load one tile ahead.  Dot products are completed over
+// the LPT lanes of a row with DPP adds (quad permutes, half-row and row
+// mirrors) and row-swap permutes; each token slot r keeps its own online
+// softmax state, folded in once per tile, and the TPW slot states are
+// merged by log-sum-exp at the end of a unit.
+// ---------------------------------------------------------------------------
+constexpr int kTileTok = 16;
+
+// Sum over aligned groups of LPT lanes (LPT a power of two <= 64).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false);
+    return v + __int_as_float(moved);
+}
+
+template <int LPT>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    if (LPT >= 2) x = dpp_add<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
+    if (LPT >= 4) x = dpp_add<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
+    if (LPT >= 8) x = dpp_add<0x141>(x);   // row_half_mirror: the other quad of 8
+    if (LPT >= 16) x = dpp_add<0x140>(x);  // row_mirror: the other half of the row
+    if (LPT >= 32) {                        // the other row of 16 (lane ^ 16)
+        const uint32_t u = __float_as_uint(x);
+        const auto rr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        x = __uint_as_float(rr[0]) + __uint_as_float(rr[1]);
+    }
+    if (LPT >= 64) {                        // the other half of the wave (lane ^ 32)
+        const uint32_t u = __float_as_uint(x);
+        const auto rr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        x = __uint_as_float(rr[0]) + __uint_as_float(rr[1]);
+    }
+    return x;
+}
+
+template <typename T, int D, int GP>
+struct VecShape {
+    static constexpr int kVec = Chunk<T>::kVec;
+    static constexpr int LPT = D / kVec;            // lanes per token row
+    static constexpr int TPW = kWave / LPT;         // rows per load instruction
+    static constexpr int PASSES = kTileTok / TPW;   // loads per lane per tile, K or V
+    static constexpr int kRow = D * (int)sizeof(T);
+    // tiles in flight while one is computed: as many as the registers allow
+    // (a tile buffer is 2 * PASSES * 4 VGPRs, the state of the heads
+    // GP * (2 kVec + 2))
+    static constexpr int kBuf = 2 * PASSES * 4, kState = GP * (2 * kVec + 2);
+    static constexpr int DEPTH = PASSES >= 8                      ? 1
+                                 : 4 * kBuf + kState <= 320 ? 3
+                                 : 3 * kBuf + kState <= 360 ? 2
+                                                            : 1;
+    static constexpr int BUFS = DEPTH + 1;
+    static constexpr bool kOk = TPW <= kTileTok;
+};
+
+template <typename T, int D, int GP>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1)))
+void decode_vector_balanced_kernel(const DecodeParams args, const int32_t *__restrict__ tables,
+                                   const int32_t *__restrict__ ctx_lens, void *__restrict__ out,
+                                   float *__restrict__ ws_m, float *__restrict__ ws_l,
+                                   float *__restrict__ ws_acc) {
+    using S = VecShape<T, D, GP>;
+    constexpr int kVec = S::kVec, LPT = S::LPT, TPW = S::TPW, PASSES = S::PASSES;
+    constexpr int kRow = S::kRow, DEPTH = S::DEPTH, BUFS = S::BUFS;
+    static_assert(S::kOk, "a tile of 16 rows must cover whole load passes");
+    // restrict arguments: the stores cannot alias the block tables, so the
+    // per-tile table reads stay on the scalar unit
+    DecodeParams p = args;
+    p.block_tables = tables;
+    p.context_lens = ctx_lens;
+    const int lane = threadIdx.x;
+    const int r = lane / LPT;                  // token slot within a pass
+    const int c = lane % LPT;                  // 16-byte chunk of head_dim
+    const int W = p.num_units;
+    const int w = xcd_remap(blockIdx.x, W);
+    const int B = p.num_seqs;
+    const int G = p.group;
+
+    // tile prefix over sequences: lane i owns sequences [i K, i K + K)
+    const int K = (B + kWave - 1) / kWave;
+    auto tiles_of = [&](int b) {
+        return (clamp_ctx(p.context_lens[b], p.max_context_len) + kTileTok - 1) / kTileTok;
+    };
+    int local = 0;
+    for (int j = 0; j < K; j++) {
+        const int b = lane * K + j;
+        if (b < B) local += tiles_of(b);
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    const int excl = incl - local;
+    const int TT = __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1));
+    const int total = TT * p.num_kv_heads;
+    const int C = (total + W - 1) / W;
+
+    const char *kbase = (const char *)p.k_cache;
+    const char *vbase = (const char *)p.v_cache;
+    const int log2bs = p.log2_block;
+    const int bs_mask = (1 << log2bs) - 1;
+    const int x1 = min(w * C + C, total);
+    int x = w * C;
+    int slot = 0;
+    while (x < x1) {
+        const int g = x / TT;
+        const int rr = x - g * TT;
+        // the sequence holding stream position rr: find its lane, then walk
+        const unsigned long long own = __ballot(rr >= excl && rr < incl);
+        const int jl = __builtin_ctzll(own);
+        int base = __builtin_amdgcn_readfirstlane(__shfl(excl, jl));
+        int b = jl * K;
+        int Tb;
+        if (K == 1) {
+            Tb = __builtin_amdgcn_readfirstlane(__shfl(local, jl));
+        } else {
+            Tb = __builtin_amdgcn_readfirstlane(tiles_of(b));
+            while (rr >= base + Tb) {
+                base += Tb;
+                b++;
+                Tb = __builtin_amdgcn_readfirstlane(tiles_of(b));
+            }
+        }
+        const int t_begin = rr - base;                 // tiles [t_begin, t_end) of unit (g, b)
+        const int t_end = min(Tb, t_begin + (x1 - x));
+        x += t_end - t_begin;
+        const int n = __builtin_amdgcn_readfirstlane(clamp_ctx(p.context_lens[b], p.max_context_len));
+
+        // q chunk c of every head of the group (zeros past G)
+        float q[GP][kVec];
+#pragma unroll
+        for (int j = 0; j < GP; j++) {
+            if (j < G) {
+                const uint4 raw = *(const uint4 *)((const T *)p.q +
+                                                   ((size_t)b * p.num_q_heads + g * G + j) * D +
+                                                   c * kVec);
+                Chunk<T>::unpack(raw, q[j]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < kVec; e++) q[j][e] = 0.f;
+            }
+        }
+        float m[GP], l[GP], acc[GP][kVec];
+#pragma unroll
+        for (int j = 0; j < GP; j++) {
+            m[j] = -INFINITY;
+            l[j] = 0.f;
+#pragma unroll
+            for (int e = 0; e < kVec; e++) acc[j][e] = 0.f;
+        }
+
+        const int32_t *__restrict__ table = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+        const int ntiles = t_end - t_begin;
+        auto phys_of = [&](int t) -> int {             // t clamped into the range
+            const int tt = t_begin + (t < ntiles ? t : ntiles - 1);
+            return table[(tt * kTileTok) >> log2bs];
+        };
+        auto load_tile = [&](int t, int phys, uint4 (&kr)[PASSES], uint4 (&vr)[PASSES]) -> int {
+            const int tok = (t_begin + t) * kTileTok;
+            const bool ok = t < ntiles && (unsigned)phys < (unsigned)p.num_blocks;
+            const int rows = ok ? min(kTileTok, n - tok) : 0;
+            const size_t off = ((((size_t)(ok ? phys : 0) * p.num_kv_heads + g) << log2bs) +
+                                (tok & bs_mask)) * (size_t)kRow;
+            const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(kbase + off), (short)0, rows * kRow, 0x00020000);
+            const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(vbase + off), (short)0, rows * kRow, 0x00020000);
+#pragma unroll
+            for (int i = 0; i < PASSES; i++) {
+                const int lo = (i * TPW + r) * kRow + c * 16;
+                kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lo, 0, 0));
+                vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lo, 0, 0));
+            }
+            return rows;
+        };
+        // fold one tile (rows visible) into the slot states
+        auto update = [&](const uint4 (&kr)[PASSES], const uint4 (&vr)[PASSES], int rows) {
+#pragma unroll
+            for (int j = 0; j < GP; j++) {
+                if (j >= G) continue;
+                float s[PASSES];
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < PASSES; i++) {
+                    float kf[kVec];
+                    Chunk<T>::unpack(kr[i], kf);
+                    float dot = 0.f;
+#pragma unroll
+                    for (int e = 0; e < kVec; e++) dot = fmaf(q[j][e], kf[e], dot);
+                    dot = lane_group_sum<LPT>(dot);
+                    s[i] = i * TPW + r < rows ? dot * p.scale_log2 : -INFINITY;
+                    tmax = fmaxf(tmax, s[i]);
+                }
+                const float m_new = fmaxf(m[j], tmax);
+                // a slot that has seen nothing keeps m = -inf: shift by 0,
+                // which makes alpha and every weight exactly 0
+                const float shift = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = fast_exp2(m[j] - shift);
+                m[j] = m_new;
+                float lsum = 0.f, pv[kVec];
+#pragma unroll
+                for (int e = 0; e < kVec; e++) pv[e] = 0.f;
+#pragma unroll
+                for (int i = 0; i < PASSES; i++) {
+                    const float pw = fast_exp2(s[i] - shift);
+                    lsum += pw;
+                    float vf[kVec];
+                    Chunk<T>::unpack(vr[i], vf);
+#pragma unroll
+                    for (int e = 0; e < kVec; e++) pv[e] = fmaf(pw, vf[e], pv[e]);
+                }
+                l[j] = fmaf(l[j], alpha, lsum);
+#pragma unroll
+                for (int e = 0; e < kVec; e++) acc[j][e] = fmaf(acc[j][e], alpha, pv[e]);
+            }
+        };
+
+        uint4 kr[BUFS][PASSES], vr[BUFS][PASSES];
+        int rows[BUFS];
+        int phys_next = phys_of(0);
+#pragma unroll
+        for (int j = 0; j < DEPTH; j++) {
+            rows[j] = load_tile(j, phys_next, kr[j], vr[j]);
+            phys_next = phys_of(j + 1);
+        }
+        for (int tb = 0; tb < ntiles; tb += BUFS) {
+#pragma unroll
+            for (int j = 0; j < BUFS; j++) {
+                const int t = tb + j;
+                if (t >= ntiles) break;
+                const int jn = (j + DEPTH) % BUFS;
+                rows[jn] = load_tile(t + DEPTH, phys_next, kr[jn], vr[jn]);
+                phys_next = phys_of(t + DEPTH + 1);
+                __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the wait
+                update(kr[j], vr[j], rows[j]);
+            }
+        }
+
+        // merge the TPW token-slot states (lanes with the same chunk c)
+#pragma unroll
+        for (int o = LPT; o < kWave; o <<= 1) {
+#pragma unroll
+            for (int j = 0; j < GP; j++) {
+                if (j >= G) continue;
+                const float m_o = __shfl_xor(m[j], o);
+                const float l_o = __shfl_xor(l[j], o);
+                const float mm = fmaxf(m[j], m_o);
+                const float fa = m[j] == -INFINITY ? 0.f : fast_exp2(m[j] - mm);
+                const float fb = m_o == -INFINITY ? 0.f : fast_exp2(m_o - mm);
+                l[j] = l[j] * fa + l_o * fb;
+#pragma unroll
+                for (int e = 0; e < kVec; e++) {
+                    const float a_o = __shfl_xor(acc[j][e], o);
+                    acc[j][e] = acc[j][e] * fa + a_o * fb;
+                }
+                m[j] = mm;
+            }
+        }
+        const bool whole = t_begin == 0 && t_end == Tb;
+        if (r == 0) {
+#pragma unroll
+            for (int j = 0; j < GP; j++) {
+                if (j >= G) continue;
+                if (whole) {
+                    const float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
+                    float o[kVec];
+#pragma unroll
+                    for (int e = 0; e < kVec; e++) o[e] = acc[j][e] * inv;
+                    Chunk<T>::pack_store((T *)out + ((size_t)b * p.num_q_heads + g * G + j) * D +
+                                             c * kVec,
+                                         o);
+                } else {
+                    const size_t prow = ((size_t)w * 2 + slot) * kMaxGroup + j;
+                    float *dst = ws_acc + prow * D + c * kVec;
+#pragma unroll
+                    for (int e = 0; e < kVec; e++) dst[e] = acc[j][e];
+                    if (c == 0) {
+                        ws_m[prow] = m[j];
+                        ws_l[prow] = l[j];
+                    }
+                }
+            }
+        }
+        // the merge kernel expects a unit that begins inside a share in
+        // slot 1, whatever the wavefront's earlier units were
+        slot = 1;
+    }
+}
+
+template <typename T, int D, int GP>
+static void launch_balanced_g(const DecodeParams &p, hipStream_t stream) {
+    if constexpr (VecShape<T, D, GP>::kOk)
+        hipLaunchKernelGGL((decode_vector_balanced_kernel<T, D, GP>), dim3(p.num_units),
+                           dim3(kWave), 0, stream, p, p.block_tables, p.context_lens, p.out,
+                           p.ws_m, p.ws_l, p.ws_acc);
+}
+
+template <typename T, int D>
+static hipError_t launch_balanced_d(const DecodeParams &p, hipStream_t stream) {
+    switch (p.group <= 1 ? 1 : p.group <= 2 ? 2 : p.group <= 4 ? 4 : p.group <= 8 ? 8 : 16) {
+    case 1: launch_balanced_g<T, D, 1>(p, stream); break;
+    case 2: launch_balanced_g<T, D, 2>(p, stream); break;
+    case 4: launch_balanced_g<T, D, 4>(p, stream); break;
+    case 8: launch_balanced_g<T, D, 8>(p, stream); break;
+    default: launch_balanced_g<T, D, 16>(p, stream); break;
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_balanced_t(const DecodeParams &p, int head_dim, hipStream_t stream) {
+    switch (head_dim) {
+    case 16: return launch_balanced_d<T, 16>(p, stream);
+    case 32: return launch_balanced_d<T, 32>(p, stream);
+    case 64: return launch_balanced_d<T, 64>(p, stream);
+    case 128: return launch_balanced_d<T, 128>(p, stream);
+    default: return launch_balanced_d<T, 256>(p, stream);
+    }
+}
+
+bool vector_balanced_supported(int head_dim, int dtype, int block_size) {
+    const int vec = dtype == 0 ? 4 : 8;
+    return block_size >= kTileTok && kWave / (head_dim / vec) <= kTileTok;
+}
+
+hipError_t launch_decode_vector_balanced(const DecodeParams &p, int head_dim, int dtype,
+                                         hipStream_t stream) {
+    if (p.num_units == 0) return hipSuccess;
+    return dtype == 0 ? launch_balanced_t<float>(p, head_dim, stream)
+                      : launch_balanced_t<uint16_t>(p, head_dim, stream);
+}
+
 template <typename T, int D>
 static hipError_t launch_d(const DecodeParams &p, hipStream_t stream) {
     const dim3 grid(p.num_units), block(kWave);

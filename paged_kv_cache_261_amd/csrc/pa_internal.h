@@ -165,6 +165,12 @@ hipError_t launch_cache_write(const void *k, const void *v, void *k_cache, void 
 
 hipError_t launch_decode_vector(const DecodeParams &p, int head_dim, int dtype,
                                 hipStream_t stream);
+// Work-balanced split on the vector ALUs (same stream, slots and merge as the
+// matrix-core balanced split); for block_size >= 16 and head dims whose
+// 16-token tile covers whole 64-lane load passes.
+bool vector_balanced_supported(int head_dim, int dtype, int block_size);
+hipError_t launch_decode_vector_balanced(const DecodeParams &p, int head_dim, int dtype,
+                                         hipStream_t stream);
 
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 

@@ -212,16 +212,26 @@ hipError_t launch_reduce(const ReduceParams &p, int dtype, hipStream_t stream) {
                       : launch_reduce_t<uint16_t>(p, lds, stream);
 }
 
+template <typename T>
+static void launch_reduce_balanced_t(const ReduceParams &p, unsigned rows, size_t lds,
+                                     hipStream_t stream) {
+    switch (p.head_dim) {
+    case 16: hipLaunchKernelGGL((reduce_balanced_kernel<T, 16>), dim3(rows), dim3(16), lds, stream, p); break;
+    case 32: hipLaunchKernelGGL((reduce_balanced_kernel<T, 32>), dim3(rows), dim3(32), lds, stream, p); break;
+    case 64: hipLaunchKernelGGL((reduce_balanced_kernel<T, 64>), dim3(rows), dim3(64), lds, stream, p); break;
+    case 128: hipLaunchKernelGGL((reduce_balanced_kernel<T, 128>), dim3(rows), dim3(128), lds, stream, p); break;
+    default: hipLaunchKernelGGL((reduce_balanced_kernel<T, 256>), dim3(rows), dim3(256), lds, stream, p); break;
+    }
+}
+
 hipError_t launch_reduce_balanced(const ReduceParams &p, int dtype, hipStream_t stream) {
     const unsigned rows = (unsigned)p.num_seqs * (unsigned)p.num_kv_heads * (unsigned)p.group;
     if (rows == 0) return hipSuccess;
     const size_t lds = (8 + (size_t)p.num_waves) * sizeof(float);   // pieces <= wavefronts
     if (dtype == 0)
-        hipLaunchKernelGGL((reduce_balanced_kernel<float, 128>), dim3(rows), dim3(128), lds,
-                           stream, p);
+        launch_reduce_balanced_t<float>(p, rows, lds, stream);
     else
-        hipLaunchKernelGGL((reduce_balanced_kernel<uint16_t, 128>), dim3(rows), dim3(128), lds,
-                           stream, p);
+        launch_reduce_balanced_t<uint16_t>(p, rows, lds, stream);
     return hipGetLastError();
 }
 

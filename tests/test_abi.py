@@ -62,12 +62,17 @@ def test_workspace_size_and_auto_partition(lib):
             ws = pa.pa_decode_workspace_size(16, 64, 8, 128, bs, ctx, -1, 1)
             assert (ws == 0) == (p == 0)
             pf = pa.pa_decode_auto_partition(16, 64, 8, 128, bs, ctx, 0)   # fp32: vector path
-            assert pf == 0 or (pf % bs == 0 and pf > 0)
+            assert pf == 0 or (pf % bs == 0 and pf > 0) or (pf == pa.PA_PARTITION_BALANCED
+                                                              and bs >= 16)
     # balanced: plan + 1024 wavefronts x 2 slots x 16 heads x (128 + 2) floats
     nb = pa.pa_decode_workspace_size(256, 32, 8, 128, 16, 4096, -2, 1)
     assert nb >= 1024 * 2 * 16 * 130 * 4
-    assert pa.pa_decode_workspace_size(256, 32, 8, 64, 16, 4096, -2, 1) == 0   # not bf16/d128
-    assert pa.pa_decode_workspace_size(256, 32, 8, 128, 16, 4096, -2, 0) == 0
+    # the vector-ALU balanced split takes the other shapes with block_size >= 16
+    assert pa.pa_decode_workspace_size(256, 32, 8, 64, 16, 4096, -2, 1) >= 1024 * 2 * 16 * 66 * 4
+    assert pa.pa_decode_workspace_size(256, 32, 8, 128, 16, 4096, -2, 0) >= nb
+    assert pa.pa_decode_workspace_size(256, 32, 8, 128, 8, 4096, -2, 1) == 0   # block_size < 16
+    assert pa.pa_decode_workspace_size(256, 32, 8, 16, 16, 4096, -2, 1) == 0   # bf16 d16
+    assert pa.pa_decode_workspace_size(256, 32, 8, 64, 16, 4096, -3, 1) == 0   # shared: bf16 d128
     assert pa.pa_decode_workspace_size(1, 1, 1, 128, 16, 100, 24, 1) == 0   # not a multiple
 
 
@@ -104,9 +109,11 @@ def decode_call(lib, fn="pa_decode", **kw):
     (dict(q=Z), NULL), (dict(bt=Z), NULL), (dict(cl=Z), NULL), (dict(out=Z), NULL),
     (dict(q=MIS), ALIGN), (dict(kc=MIS), ALIGN), (dict(algo=7), ALGO),
     (dict(algo=2, dtype=0), ALGO), (dict(algo=2, d=64), ALGO), (dict(algo=2, bs=8, MB=16), ALGO),
-    (dict(part=24), SHAPE), (dict(part=-4), SHAPE), (dict(part=-2, dtype=0, d=64), ALGO),
+    (dict(part=24), SHAPE), (dict(part=-4), SHAPE), (dict(part=-2, dtype=0, d=64), WS),
+    (dict(part=-2, bs=8, MB=16), ALGO), (dict(part=-2, dtype=1, d=16), ALGO),
+    (dict(part=-2, algo=2, dtype=0), ALGO),
     (dict(part=-3, dtype=0), ALGO), (dict(part=-3, algo=1), ALGO), (dict(part=-3), WS),
-    (dict(part=-2, algo=1), ALGO), (dict(part=-2), WS),
+    (dict(part=-2, algo=1), WS), (dict(part=-2), WS),
     (dict(part=32), WS), (dict(part=32, ws=A, wsb=16), WS), (dict(part=-1, max_ctx=1024, MB=64), WS),
 ])
 def test_decode_rejects_bad_arguments(lib, kw, status):
@@ -139,7 +146,8 @@ def test_reduce_rejects_bad_arguments(lib):
     assert lib.pa_decode_reduce(A, A, 2, 8, 2, 128, 1000, 0, A, 1 << 20, 1, Z) == SHAPE
     assert lib.pa_decode_reduce(A, A, 2, 8, 3, 128, 1000, 512, A, 1 << 20, 1, Z) == SHAPE
     assert lib.pa_decode_reduce(A, A, 2, 8, 2, 100, 1000, 512, A, 1 << 20, 1, Z) == UNSUP
-    assert lib.pa_decode_reduce(A, A, 2, 8, 2, 64, 1000, -2, A, 1 << 30, 1, Z) == UNSUP
+    assert lib.pa_decode_reduce(A, A, 2, 34, 2, 64, 1000, -2, A, 1 << 30, 1, Z) == UNSUP
+    assert lib.pa_decode_reduce(A, A, 2, 8, 2, 64, 1000, -3, A, 1 << 30, 1, Z) == UNSUP
     assert lib.pa_decode_reduce(A, A, 2, 8, 2, 128, 1000, 512, A, 16, 1, Z) == WS
     assert lib.pa_decode_reduce(A, A, 2, 8, 2, 128, 1000, -2, A, 4096, 1, Z) == WS
     assert lib.pa_decode_reduce(Z, A, 2, 8, 2, 128, 1000, 512, A, 1 << 20, 1, Z) == NULL

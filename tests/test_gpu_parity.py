@@ -118,6 +118,8 @@ def modes_for(cfg):
     else:
         algos = [MFMA, VECTOR]
     parts = [0, -1, 512 if cfg.block_size <= 512 else cfg.block_size, 4 * cfg.block_size]
+    if cfg.block_size >= 16:
+        parts.append(pa.PA_PARTITION_BALANCED)
     return [(a, p) for a in algos for p in parts]
 
 
@@ -145,7 +147,7 @@ def test_full_size_sampled(name):
     bench_part = w.cfg.partition_size        # the launch configuration the benchmark times
     BAL, SHR = pa.PA_PARTITION_BALANCED, pa.PA_PARTITION_SHARED
     for algo, part in [(AUTO, bench_part), (AUTO, -1), (MFMA, BAL), (MFMA, SHR), (MFMA, 0),
-                       (MFMA, 512), (VECTOR, 512), (MFMA, 256)]:
+                       (MFMA, 512), (VECTOR, 512), (MFMA, 256), (VECTOR, BAL)]:
         note(f"[gpu parity] {name} algo {algo} partition {part}")
         got = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, mc, part, algo)
         H.assert_close_to_oracle(got[idx], ref, "bf16", f"{name} algo {algo} partition {part}")
@@ -198,6 +200,9 @@ def needle_case(dtype, hq, hkv, d, bs, ctxs, c, seed):
     ("bf16", MFMA, 32, 8, 128, 16, -3), ("bf16", MFMA, 64, 8, 128, 64, -3),
     ("bf16", MFMA, 16, 16, 128, 32, -3), ("bf16", VECTOR, 32, 8, 128, 16, 512), ("f32", VECTOR, 8, 8, 64, 16, 0),
     ("f32", VECTOR, 4, 4, 16, 4, 8), ("f32", VECTOR, 12, 4, 32, 1, 0),
+    ("f32", VECTOR, 8, 8, 64, 16, -2), ("bf16", VECTOR, 32, 8, 128, 16, -2),
+    ("f32", VECTOR, 12, 4, 32, 32, -2), ("bf16", VECTOR, 16, 4, 64, 64, -2),
+    ("f32", VECTOR, 4, 4, 16, 16, -2), ("f32", VECTOR, 2, 2, 256, 16, -2),
 ])
 def test_needle_is_bit_exact(dtype, algo, hq, hkv, d, bs, part):
     """q = c e0, K = 0 but K[needle, 0] = c: the softmax is one-hot in float32
@@ -222,7 +227,7 @@ def test_one_token_and_empty_context(dtype, algo):
     vl = [S._normal(rng, (n, hkv, d), dtype) for n in (1, 1, 5)]
     kc, vc, tab = H.paginate(kl, vl, bs, 8, rng, dtype)
     ctx = np.array([1, 0, 1], dtype=np.int32)
-    for part in ((0, 16, -2, -3) if algo == MFMA else (0, 16)):
+    for part in ((0, 16, -2, -3) if algo == MFMA else (0, 16, -2)):
         got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, ctx, 0.3, 5, part, algo)
         np.testing.assert_array_equal(got[0], np.repeat(H.to_float(vl[0][0], dtype), 4, axis=0))
         assert (got[1] == 0).all()
@@ -256,7 +261,8 @@ def test_every_block_size(dtype, algo, bs):
     nb = sum((n + bs - 1) // bs for n in ctxs) + 5
     kc, vc, tab = H.paginate(kl, vl, bs, nb, rng, dtype)
     ref = pao.decode_concat(q, kc, vc, tab, np.array(ctxs), 1 / math.sqrt(d))
-    for part in (0, -1, max(bs, 256)) + ((-3,) if algo == MFMA else ()):
+    for part in (0, -1, max(bs, 256)) + ((-3,) if algo == MFMA else ()) + \
+            ((-2,) if bs >= 16 else ()):
         got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, np.array(ctxs), 1 / math.sqrt(d),
                            None, part, algo)
         H.assert_close_to_oracle(got, ref, dtype, f"bs {bs} partition {part}")
@@ -275,6 +281,30 @@ def test_every_head_dim_vector(d, dtype):
     ref = pao.decode_concat(q, kc, vc, tab, np.array(ctxs), 0.2)
     got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, np.array(ctxs), 0.2, None, 16, VECTOR)
     H.assert_close_to_oracle(got, ref, dtype, f"head_dim {d}")
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [1, 3, 16])
+def test_vector_balanced_split(d, dtype, G):
+    """The work-balanced split on the vector ALUs: every head dim and dtype it
+    takes (a 16-token tile must cover whole load passes: not bf16 d16), group
+    sizes up to 16, contexts that end mid-tile, an empty one, and enough
+    tokens that the 1024 wavefront shares cut through sequences."""
+    if dtype == "bf16" and d == 16:
+        pytest.skip("a bf16 head_dim-16 row is 32 bytes: 32 rows per load pass > one tile")
+    rng = np.random.default_rng(d * 31 + G)
+    ctxs = [0, 1, 17, 300, 2500, 999, 20000]  # 1484 tiles per KV head: ~3 per wavefront
+    hkv = 2
+    q = S._normal(rng, (len(ctxs), hkv * G, d), dtype)
+    kl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    vl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    kc, vc, tab = H.paginate(kl, vl, 16, 1500, rng, dtype)
+    ref = pao.decode_concat(q, kc, vc, tab, np.array(ctxs), 1 / math.sqrt(d))
+    got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, np.array(ctxs), 1 / math.sqrt(d),
+                       None, pa.PA_PARTITION_BALANCED, VECTOR)
+    assert (got[0] == 0).all()
+    H.assert_close_to_oracle(got, ref, dtype, f"vector balanced d {d} {dtype} G {G}")
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 16])
@@ -333,7 +363,7 @@ def test_physical_placement_and_repeats_do_not_change_bits(dtype, algo):
     kl = [S._normal(rng, (n, 4, 128), dtype) for n in ctxs]
     vl = [S._normal(rng, (n, 4, 128), dtype) for n in ctxs]
     outs = []
-    parts = (0, 512, -2, -3) if algo == MFMA else (0, 512)
+    parts = (0, 512, -2, -3) if algo == MFMA else (0, 512, -2)
     for seed in (10, 11):
         kc, vc, tab = H.paginate(kl, vl, 16, 200, np.random.default_rng(seed), dtype)
         kd, vd = H.to_dev(kc), H.to_dev(vc)
