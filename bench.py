@@ -45,7 +45,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 DEFAULT_CONFIG = "gqa_bf16"
 KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_shared.hip", "pa_decode_vector.hip",
                   "pa_reduce.hip", "pa_cache_write.hip", "pa_api.cpp", "pa_internal.h",
-                  "pa_mfma_tile.h"]
+                  "pa_mfma_tile.h", "pa_copy_blocks.hip", "pa_prefill.hip"]
 
 
 def log(msg):
@@ -89,7 +89,7 @@ def decode_kernel_name(c, part, algo):
     if part == -3:
         return "decode_shared_kernel (after plan_shared_kernel)"
     if not mfma:
-        return "decode_vector_kernel"
+        return "decode_vector_balanced_kernel" if part == -2 else "decode_vector_kernel"
     return "decode_mfma_kernel" if part == 0 else "decode_mfma_balanced_kernel"
 
 

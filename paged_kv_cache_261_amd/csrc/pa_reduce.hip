@@ -111,6 +111,9 @@ __global__ __launch_bounds__(D) void reduce_kernel(const ReduceParams p) {
                     p.ws_acc + prow * D, D, lds + 8, lds);
 }
 
+// Units cut into at most this many pieces are merged in registers.
+constexpr int kDirectPieces = 8;
+
 // Work-balanced split: one workgroup per (sequence, KV head, head of the
 // group).  The split is re-derived from the context lengths exactly as the
 // decode kernel made it: sequence b contributes T_b = ceil(n_b / 16) tiles
@@ -130,15 +133,23 @@ __global__ __launch_bounds__(D) void reduce_balanced_kernel(const ReduceParams p
     const int b = unit / p.num_kv_heads;
     const int g = unit % p.num_kv_heads;
     constexpr int kTileTokens = 16;
+    // every wavefront of the workgroup sums the tile counts itself (no
+    // barrier): lanes of width kW stride over the sequences
+    constexpr int kW = D < kWave ? D : kWave;
+    const int lane = threadIdx.x % kW;
     int before = 0, all = 0;
-    for (int s = threadIdx.x; s < p.num_seqs; s += D) {
+    for (int s = lane; s < p.num_seqs; s += kW) {
         const int t = (clamp_ctx(p.context_lens[s], p.max_context_len) + kTileTokens - 1) /
                       kTileTokens;
         all += t;
         if (s < b) before += t;
     }
-    const int S = block_sum<D>(before, (int *)lds);
-    const int TT = block_sum<D>(all, (int *)lds);
+#pragma unroll
+    for (int o = kW / 2; o >= 1; o >>= 1) {
+        before += __shfl_xor(before, o, kW);
+        all += __shfl_xor(all, o, kW);
+    }
+    const int S = before, TT = all;
     const int Tb = (clamp_ctx(p.context_lens[b], p.max_context_len) + kTileTokens - 1) /
                    kTileTokens;
     const int C = (TT * p.num_kv_heads + p.num_waves - 1) / p.num_waves;
@@ -152,27 +163,60 @@ __global__ __launch_bounds__(D) void reduce_balanced_kernel(const ReduceParams p
     if (first == last) return;                  // finished by its wavefront
     // pieces are wavefronts first..last; wavefront first's piece sits in
     // slot 1 unless the unit began exactly at its share's start, the rest
-    // in slot 0: piece q lives at row ((first + q) * 2 + slot) * 16 + j
+    // in slot 0: piece 0 at row r0, piece q >= 1 at row r1 + 2*16*(q-1)
     const int slot0 = start != first * C ? 1 : 0;
     const size_t r0 = ((size_t)first * 2 + slot0) * kMaxGroup + j;
+    const size_t r1 = ((size_t)(first + 1) * 2) * kMaxGroup + j;
     const int n = last - first + 1;
+    const int i = threadIdx.x;
+    auto row_of = [&](int q) -> size_t {
+        return q == 0 ? r0 : r1 + (size_t)(q - 1) * 2 * kMaxGroup;
+    };
+    if (n <= kDirectPieces) {
+        // every thread loads every piece's m and l (one broadcast address
+        // per piece) with its own accumulator element, all at once, and
+        // merges in registers: one round trip, no barrier
+        float mq[kDirectPieces], lq[kDirectPieces], aq[kDirectPieces];
+#pragma unroll
+        for (int q = 0; q < kDirectPieces; q++) {
+            if (q < n) {
+                const size_t rq = row_of(q);
+                mq[q] = p.ws_m[rq];
+                lq[q] = p.ws_l[rq];
+                aq[q] = p.ws_acc[rq * D + i];
+            }
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kDirectPieces; q++)
+            if (q < n) M = fmaxf(M, mq[q]);
+        float num = 0.f, den = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int q = 0; q < kDirectPieces; q++) {
+                if (q < n && mq[q] != -INFINITY) {   // empty piece: weight 0, not read
+                    const float wq = __builtin_amdgcn_exp2f(mq[q] - M);
+                    den = fmaf(wq, lq[q], den);
+                    num = fmaf(wq, aq[q], num);
+                }
+            }
+        }
+        store_out(out + i, den > 0.f ? num / den : 0.f);
+        return;
+    }
     if (slot0 == 0) {
         // uniform stride 2 * 16 rows between consecutive pieces
         merge_row<T, D>(out, n, p.ws_m + r0, p.ws_l + r0, 2 * kMaxGroup, p.ws_acc + r0 * D,
                         (size_t)2 * kMaxGroup * D, lds + 8, lds);
     } else {
-        // the first piece is one slot further than the stride predicts:
-        // merge it through a shifted view (rows r0 and r0 + 16 + 2*16*(q-1))
-        const size_t r1 = ((size_t)(first + 1) * 2) * kMaxGroup + j;
-        const int i = threadIdx.x;
+        // the first piece is one slot further than the stride predicts
         float *red = lds, *weights = lds + 8;
         float mx = p.ws_m[r0];
-        for (int q = 1 + i; q < n; q += D)
-            mx = fmaxf(mx, p.ws_m[r1 + (size_t)(q - 1) * 2 * kMaxGroup]);
+        for (int q = 1 + i; q < n; q += D) mx = fmaxf(mx, p.ws_m[row_of(q)]);
         const float M = block_max<D>(mx, red);
         float dl = 0.f;
         for (int q = i; q < n; q += D) {
-            const size_t rq = q == 0 ? r0 : r1 + (size_t)(q - 1) * 2 * kMaxGroup;
+            const size_t rq = row_of(q);
             const float mq = p.ws_m[rq];
             const float wq = (mq == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mq - M);
             weights[q] = wq;
