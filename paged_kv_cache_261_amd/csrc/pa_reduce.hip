@@ -114,62 +114,30 @@ __global__ __launch_bounds__(D) void reduce_kernel(const ReduceParams p) {
 // Units cut into at most this many pieces are merged in registers.
 constexpr int kDirectPieces = 8;
 
-// Work-balanced split: one workgroup per (sequence, KV head, head of the
-// group).  The split is re-derived from the context lengths exactly as the
-// decode kernel made it: sequence b contributes T_b = ceil(n_b / 16) tiles
-// per KV head, S_b = sum_{b' < b} T_b', TT = sum_b T_b, and each of the W
-// wavefronts owned C = ceil(Hkv TT / W) consecutive tiles of the stream
-// (KV head slowest, then sequence, then tile).  Unit (g, b) spans
-// [g TT + S_b, g TT + S_b + T_b); if one wavefront covered it whole, that
-// wavefront wrote the output.  Otherwise wavefronts first..last each hold a
-// piece: wavefront `first` in slot 1 when the unit began inside its share
-// (slot 0 when exactly at its start), every later one in slot 0.  An empty
-// context gives zeros.
+// Work-balanced split.  The split is re-derived from the context lengths
+// exactly as the decode kernels made it: sequence b contributes
+// T_b = ceil(n_b / 16) tiles per KV head, S_b = sum_{b' < b} T_b',
+// TT = sum_b T_b, and each of the W wavefronts owned C = ceil(Hkv TT / W)
+// consecutive tiles of the stream (KV head slowest, then sequence, then
+// tile).  Unit (g, b) spans [g TT + S_b, g TT + S_b + T_b); if one
+// wavefront covered it whole, that wavefront wrote the output.  Otherwise
+// wavefronts first..last each hold a piece: wavefront `first` in slot 1 when
+// the unit began inside its share (slot 0 when exactly at its start), every
+// later one in slot 0.  An empty context gives zeros.
+constexpr int kTileTokens = 16;
+
+// Merge the pieces of a unit that starts at stream position `start` and
+// spans wavefronts first..last (first < last), for head j of the group,
+// into out (head_dim values; thread i writes element i).
 template <typename T, int D>
-__global__ __launch_bounds__(D) void reduce_balanced_kernel(const ReduceParams p) {
-    extern __shared__ float lds[];
-    const int j = blockIdx.x % p.group;
-    const int unit = blockIdx.x / p.group;
-    const int b = unit / p.num_kv_heads;
-    const int g = unit % p.num_kv_heads;
-    constexpr int kTileTokens = 16;
-    // every wavefront of the workgroup sums the tile counts itself (no
-    // barrier): lanes of width kW stride over the sequences
-    constexpr int kW = D < kWave ? D : kWave;
-    const int lane = threadIdx.x % kW;
-    int before = 0, all = 0;
-    for (int s = lane; s < p.num_seqs; s += kW) {
-        const int t = (clamp_ctx(p.context_lens[s], p.max_context_len) + kTileTokens - 1) /
-                      kTileTokens;
-        all += t;
-        if (s < b) before += t;
-    }
-#pragma unroll
-    for (int o = kW / 2; o >= 1; o >>= 1) {
-        before += __shfl_xor(before, o, kW);
-        all += __shfl_xor(all, o, kW);
-    }
-    const int S = before, TT = all;
-    const int Tb = (clamp_ctx(p.context_lens[b], p.max_context_len) + kTileTokens - 1) /
-                   kTileTokens;
-    const int C = (TT * p.num_kv_heads + p.num_waves - 1) / p.num_waves;
-    T *out = (T *)p.out + ((size_t)b * p.num_q_heads + (size_t)g * p.group + j) * D;
-    if (Tb == 0) {
-        store_out(out + threadIdx.x, 0.f);
-        return;
-    }
-    const int start = g * TT + S;
-    const int first = start / C, last = (start + Tb - 1) / C;
-    if (first == last) return;                  // finished by its wavefront
-    // pieces are wavefronts first..last; wavefront first's piece sits in
-    // slot 1 unless the unit began exactly at its share's start, the rest
-    // in slot 0: piece 0 at row r0, piece q >= 1 at row r1 + 2*16*(q-1)
+__device__ __forceinline__ void merge_unit_row(const ReduceParams &p, T *out, int start,
+                                               int first, int last, int C, int j, float *lds) {
     const int slot0 = start != first * C ? 1 : 0;
     const size_t r0 = ((size_t)first * 2 + slot0) * kMaxGroup + j;
     const size_t r1 = ((size_t)(first + 1) * 2) * kMaxGroup + j;
     const int n = last - first + 1;
     const int i = threadIdx.x;
-    auto row_of = [&](int q) -> size_t {
+    auto row_of = [&](int q) -> size_t {   // piece 0 at r0, piece q >= 1 at r1 + 2*16*(q-1)
         return q == 0 ? r0 : r1 + (size_t)(q - 1) * 2 * kMaxGroup;
     };
     if (n <= kDirectPieces) {
@@ -208,31 +176,194 @@ __global__ __launch_bounds__(D) void reduce_balanced_kernel(const ReduceParams p
         // uniform stride 2 * 16 rows between consecutive pieces
         merge_row<T, D>(out, n, p.ws_m + r0, p.ws_l + r0, 2 * kMaxGroup, p.ws_acc + r0 * D,
                         (size_t)2 * kMaxGroup * D, lds + 8, lds);
-    } else {
-        // the first piece is one slot further than the stride predicts
-        float *red = lds, *weights = lds + 8;
-        float mx = p.ws_m[r0];
-        for (int q = 1 + i; q < n; q += D) mx = fmaxf(mx, p.ws_m[row_of(q)]);
-        const float M = block_max<D>(mx, red);
-        float dl = 0.f;
-        for (int q = i; q < n; q += D) {
-            const size_t rq = row_of(q);
-            const float mq = p.ws_m[rq];
-            const float wq = (mq == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mq - M);
-            weights[q] = wq;
-            dl = fmaf(wq, p.ws_l[rq], dl);
-        }
-        const float den = block_sum<D>(dl, red);
-        if (D <= kWave) __syncthreads();
-        float num = 0.f;
-        if (M != -INFINITY) {
-            num = weights[0] * p.ws_acc[r0 * D + i];
-            const float *a = p.ws_acc + r1 * D + i;
+        return;
+    }
+    // the first piece is one slot further than the stride predicts
+    float *red = lds, *weights = lds + 8;
+    float mx = p.ws_m[r0];
+    for (int q = 1 + i; q < n; q += D) mx = fmaxf(mx, p.ws_m[row_of(q)]);
+    const float M = block_max<D>(mx, red);
+    float dl = 0.f;
+    for (int q = i; q < n; q += D) {
+        const size_t rq = row_of(q);
+        const float mq = p.ws_m[rq];
+        const float wq = (mq == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mq - M);
+        weights[q] = wq;
+        dl = fmaf(wq, p.ws_l[rq], dl);
+    }
+    const float den = block_sum<D>(dl, red);
+    if (D <= kWave) __syncthreads();
+    float num = 0.f;
+    if (M != -INFINITY) {
+        num = weights[0] * p.ws_acc[r0 * D + i];
+        const float *a = p.ws_acc + r1 * D + i;
 #pragma unroll 8
-            for (int q = 1; q < n; q++)
-                num = fmaf(weights[q], a[(size_t)(q - 1) * 2 * kMaxGroup * D], num);
+        for (int q = 1; q < n; q++)
+            num = fmaf(weights[q], a[(size_t)(q - 1) * 2 * kMaxGroup * D], num);
+    }
+    store_out(out + i, den > 0.f ? num / den : 0.f);
+}
+
+// The register merge for JB heads j0 .. j0+JB-1 of a unit cut into
+// n <= kDirectPieces pieces (heads past the group are skipped): all loads
+// are issued before the first store.  out0: the output row of head j0.
+template <typename T, int D, int JB>
+__device__ __forceinline__ void merge_unit_rows_direct(const ReduceParams &p, T *out0, int start,
+                                                       int first, int last, int C, int j0) {
+    const int slot0 = start != first * C ? 1 : 0;
+    const int n = last - first + 1;
+    const int i = threadIdx.x;
+    float mq[JB][kDirectPieces], lq[JB][kDirectPieces], aq[JB][kDirectPieces];
+#pragma unroll
+    for (int jj = 0; jj < JB; jj++) {
+        const int j = j0 + jj;
+#pragma unroll
+        for (int q = 0; q < kDirectPieces; q++) {
+            if (q < n && j < p.group) {
+                const size_t rq =
+                    (q == 0 ? ((size_t)first * 2 + slot0) : ((size_t)(first + q) * 2)) * kMaxGroup + j;
+                mq[jj][q] = p.ws_m[rq];
+                lq[jj][q] = p.ws_l[rq];
+                aq[jj][q] = p.ws_acc[rq * D + i];
+            }
         }
-        store_out(out + i, den > 0.f ? num / den : 0.f);
+    }
+#pragma unroll
+    for (int jj = 0; jj < JB; jj++) {
+        if (j0 + jj >= p.group) break;
+        float M = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kDirectPieces; q++)
+            if (q < n) M = fmaxf(M, mq[jj][q]);
+        float num = 0.f, den = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int q = 0; q < kDirectPieces; q++) {
+                if (q < n && mq[jj][q] != -INFINITY) {   // empty piece: weight 0, not read
+                    const float wq = __builtin_amdgcn_exp2f(mq[jj][q] - M);
+                    den = fmaf(wq, lq[jj][q], den);
+                    num = fmaf(wq, aq[jj][q], num);
+                }
+            }
+        }
+        store_out(out0 + (size_t)jj * D + i, den > 0.f ? num / den : 0.f);
+    }
+}
+
+__device__ __forceinline__ int tiles_of_seq(const ReduceParams &p, int s) {
+    return (clamp_ctx(p.context_lens[s], p.max_context_len) + kTileTokens - 1) / kTileTokens;
+}
+
+// One workgroup per (sequence, KV head, head of the group) row.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void reduce_balanced_kernel(const ReduceParams p) {
+    extern __shared__ float lds[];
+    const int j = blockIdx.x % p.group;
+    const int unit = blockIdx.x / p.group;
+    const int b = unit / p.num_kv_heads;
+    const int g = unit % p.num_kv_heads;
+    // every wavefront of the workgroup sums the tile counts itself (no
+    // barrier): lanes of width kW stride over the sequences
+    constexpr int kW = D < kWave ? D : kWave;
+    const int lane = threadIdx.x % kW;
+    int before = 0, all = 0;
+    for (int s = lane; s < p.num_seqs; s += kW) {
+        const int t = tiles_of_seq(p, s);
+        all += t;
+        if (s < b) before += t;
+    }
+#pragma unroll
+    for (int o = kW / 2; o >= 1; o >>= 1) {
+        before += __shfl_xor(before, o, kW);
+        all += __shfl_xor(all, o, kW);
+    }
+    const int S = before, TT = all;
+    const int Tb = tiles_of_seq(p, b);
+    const int C = (TT * p.num_kv_heads + p.num_waves - 1) / p.num_waves;
+    T *out = (T *)p.out + ((size_t)b * p.num_q_heads + (size_t)g * p.group + j) * D;
+    if (Tb == 0) {
+        store_out(out + threadIdx.x, 0.f);
+        return;
+    }
+    const int start = g * TT + S;
+    const int first = start / C, last = (start + Tb - 1) / C;
+    if (first == last) return;                  // finished by its wavefront
+    merge_unit_row<T, D>(p, out, start, first, last, C, j, lds);
+}
+
+// The same merge indexed by wavefront boundary, for batches with many more
+// rows than wavefronts: only units that a boundary cuts need work, and each
+// is handled by the workgroup of the first boundary inside it (boundary
+// wb = 1..W-1 sits at stream position wb C), all heads of its group in
+// turn.  The last ceil(B / 8) workgroups write zeros for empty contexts,
+// 8 sequences each.
+constexpr int kZeroSeqsPerGroup = 8;
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void reduce_boundary_kernel(const ReduceParams p) {
+    extern __shared__ float lds[];
+    const int W = p.num_waves;
+    const int B = p.num_seqs;
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x >= W - 1) {
+        const int s0 = ((int)blockIdx.x - (W - 1)) * kZeroSeqsPerGroup;
+        for (int s = s0; s < min(B, s0 + kZeroSeqsPerGroup); s++) {
+            if (tiles_of_seq(p, s) != 0) continue;
+            T *o = (T *)p.out + (size_t)s * p.num_q_heads * D;
+            for (int e = tid; e < p.num_q_heads * D; e += D) store_out(o + e, 0.f);
+        }
+        return;
+    }
+    const int wb = blockIdx.x + 1;
+    // tile prefix over sequences, per wavefront: lane i owns sequences
+    // [i K, i K + K)
+    constexpr int kW = D < kWave ? D : kWave;
+    const int lane = tid % kW;
+    const int K = (B + kW - 1) / kW;
+    int local = 0;
+    for (int k = 0; k < K; k++) {
+        const int s = lane * K + k;
+        if (s < B) local += tiles_of_seq(p, s);
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < kW; off <<= 1) {
+        const int y = __shfl_up(incl, off, kW);
+        if (lane >= off) incl += y;
+    }
+    const int excl = incl - local;
+    const int TT = __shfl(incl, kW - 1, kW);
+    const int total = TT * p.num_kv_heads;
+    const int C = (total + W - 1) / W;
+    const int x = wb * C;
+    if (x >= total) return;
+    const int g = x / TT;
+    const int r = x - g * TT;
+    // the sequence holding position r: its lane, then a walk
+    const unsigned long long own = __ballot(r >= excl && r < incl);
+    const int jl = __builtin_ctzll(own) % kW;
+    int base = __shfl(excl, jl, kW);
+    int b = jl * K;
+    int Tb = tiles_of_seq(p, b);
+    while (r >= base + Tb) {
+        base += Tb;
+        b++;
+        Tb = tiles_of_seq(p, b);
+    }
+    const int start = g * TT + base;
+    // the unit starts here (not cut), or an earlier boundary cuts it
+    if (start == x || start < (wb - 1) * C) return;
+    const int first = wb - 1, last = (start + Tb - 1) / C;
+    T *out = (T *)p.out + ((size_t)b * p.num_q_heads + (size_t)g * p.group) * D;
+    if (last - first + 1 <= kDirectPieces) {
+        constexpr int JB = 4;                     // heads merged per round of loads
+        for (int j0 = 0; j0 < p.group; j0 += JB)
+            merge_unit_rows_direct<T, D, JB>(p, out + (size_t)j0 * D, start, first, last, C, j0);
+        return;
+    }
+    for (int j = 0; j < p.group; j++) {
+        merge_unit_row<T, D>(p, out + (size_t)j * D, start, first, last, C, j, lds);
+        __syncthreads();                          // lds is reused by the next head
     }
 }
 
@@ -256,15 +387,27 @@ hipError_t launch_reduce(const ReduceParams &p, int dtype, hipStream_t stream) {
                       : launch_reduce_t<uint16_t>(p, lds, stream);
 }
 
+template <typename T, int D>
+static void launch_reduce_balanced_d(const ReduceParams &p, size_t lds, hipStream_t stream) {
+    const unsigned rows = (unsigned)p.num_seqs * (unsigned)p.num_kv_heads * (unsigned)p.group;
+    if (rows > (unsigned)p.num_waves) {
+        // by boundary: W - 1 cut points plus the empty-context zeroing groups
+        const unsigned groups = (unsigned)(p.num_waves - 1) +
+                                (unsigned)((p.num_seqs + kZeroSeqsPerGroup - 1) / kZeroSeqsPerGroup);
+        hipLaunchKernelGGL((reduce_boundary_kernel<T, D>), dim3(groups), dim3(D), lds, stream, p);
+    } else {
+        hipLaunchKernelGGL((reduce_balanced_kernel<T, D>), dim3(rows), dim3(D), lds, stream, p);
+    }
+}
+
 template <typename T>
-static void launch_reduce_balanced_t(const ReduceParams &p, unsigned rows, size_t lds,
-                                     hipStream_t stream) {
+static void launch_reduce_balanced_t(const ReduceParams &p, size_t lds, hipStream_t stream) {
     switch (p.head_dim) {
-    case 16: hipLaunchKernelGGL((reduce_balanced_kernel<T, 16>), dim3(rows), dim3(16), lds, stream, p); break;
-    case 32: hipLaunchKernelGGL((reduce_balanced_kernel<T, 32>), dim3(rows), dim3(32), lds, stream, p); break;
-    case 64: hipLaunchKernelGGL((reduce_balanced_kernel<T, 64>), dim3(rows), dim3(64), lds, stream, p); break;
-    case 128: hipLaunchKernelGGL((reduce_balanced_kernel<T, 128>), dim3(rows), dim3(128), lds, stream, p); break;
-    default: hipLaunchKernelGGL((reduce_balanced_kernel<T, 256>), dim3(rows), dim3(256), lds, stream, p); break;
+    case 16: launch_reduce_balanced_d<T, 16>(p, lds, stream); break;
+    case 32: launch_reduce_balanced_d<T, 32>(p, lds, stream); break;
+    case 64: launch_reduce_balanced_d<T, 64>(p, lds, stream); break;
+    case 128: launch_reduce_balanced_d<T, 128>(p, lds, stream); break;
+    default: launch_reduce_balanced_d<T, 256>(p, lds, stream); break;
     }
 }
 
@@ -273,9 +416,9 @@ hipError_t launch_reduce_balanced(const ReduceParams &p, int dtype, hipStream_t 
     if (rows == 0) return hipSuccess;
     const size_t lds = (8 + (size_t)p.num_waves) * sizeof(float);   // pieces <= wavefronts
     if (dtype == 0)
-        launch_reduce_balanced_t<float>(p, rows, lds, stream);
+        launch_reduce_balanced_t<float>(p, lds, stream);
     else
-        launch_reduce_balanced_t<uint16_t>(p, rows, lds, stream);
+        launch_reduce_balanced_t<uint16_t>(p, lds, stream);
     return hipGetLastError();
 }
 

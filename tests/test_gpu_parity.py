@@ -307,6 +307,30 @@ def test_vector_balanced_split(d, dtype, G):
     H.assert_close_to_oracle(got, ref, dtype, f"vector balanced d {d} {dtype} G {G}")
 
 
+@pytest.mark.parametrize("dtype,algo,d", [("bf16", MFMA, 128), ("f32", VECTOR, 64),
+                                          ("bf16", VECTOR, 32)])
+def test_balanced_merge_by_boundary(dtype, algo, d):
+    """More (sequence, query head) rows than wavefronts: the merge runs per
+    wavefront boundary.  Empty contexts (zeros), units cut into 2..8 pieces
+    (merged in registers) and one cut into hundreds (merged through LDS),
+    against the oracle."""
+    rng = np.random.default_rng(d + len(dtype))
+    hkv, G = 2, 16
+    ctxs = [0, 5, 16, 17, 0, 300] * 6 + [20000, 0, 999, 64]   # 40 sequences -> 1280 rows
+    q = S._normal(rng, (len(ctxs), hkv * G, d), dtype)
+    kl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    vl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    nb = sum((n + 15) // 16 for n in ctxs) + 8
+    kc, vc, tab = H.paginate(kl, vl, 16, nb, rng, dtype)
+    ref = pao.decode_concat(q, kc, vc, tab, np.array(ctxs), 1 / math.sqrt(d))
+    got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), tab, np.array(ctxs), 1 / math.sqrt(d),
+                       None, pa.PA_PARTITION_BALANCED, algo)
+    for b, n in enumerate(ctxs):
+        if n == 0:
+            assert (got[b] == 0).all()
+    H.assert_close_to_oracle(got, ref, dtype, f"boundary merge {dtype} d {d}")
+
+
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 16])
 def test_group_sizes_mfma(G):
     rng = np.random.default_rng(G)
