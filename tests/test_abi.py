@@ -32,7 +32,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"pa_reshape_and_cache", "pa_decode", "pa_decode_partitions",
                           "pa_decode_reduce", "pa_decode_workspace_size",
-                          "pa_decode_auto_partition", "pa_status_string", "pa_copy_blocks"}
+                          "pa_decode_auto_partition", "pa_status_string", "pa_copy_blocks",
+                          "pa_prefill"}
     raw = C.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), n
@@ -169,3 +170,24 @@ def test_reduce_rejects_bad_arguments(lib):
 ])
 def test_copy_blocks_rejects_bad_arguments(lib, args, status):
     assert lib.pa_copy_blocks(*args) == status
+
+
+def prefill_call(lib, **kw):
+    a = dict(out=A, q=A, kc=A, vc=A, bt=A, cu=A, cl=A, B=2, Hq=8, Hkv=2, d=128, NB=64, bs=16,
+             MB=8, max_ctx=100, max_q=50, scale=0.1, dtype=1, stream=Z)
+    a.update(kw)
+    return lib.pa_prefill(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cu"], a["cl"], a["B"],
+                          a["Hq"], a["Hkv"], a["d"], a["NB"], a["bs"], a["MB"], a["max_ctx"],
+                          a["max_q"], C.c_float(a["scale"]), a["dtype"], a["stream"])
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), UNSUP), (dict(dtype=0), UNSUP), (dict(bs=8, MB=16), UNSUP),
+    (dict(Hq=34, Hkv=2), UNSUP), (dict(Hq=6, Hkv=4), SHAPE), (dict(B=-1), SHAPE),
+    (dict(max_ctx=8 * 16 + 1), SHAPE), (dict(max_q=101), SHAPE),
+    (dict(q=Z), NULL), (dict(cu=Z), NULL), (dict(out=MIS), ALIGN),
+    (dict(B=0, q=Z, out=Z), OK), (dict(max_q=0, q=Z, out=Z), OK),
+])
+def test_prefill_rejects_bad_arguments(lib, kw, status):
+    assert prefill_call(lib, **kw) == status
