@@ -154,8 +154,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // Launchers: validate nothing (pa_api.cpp does), enqueue, return hipError_t.
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
-// query-head columns one prefill wavefront serves (two 16-column groups)
-constexpr int kPrefillColumns = 32;
+// query-head columns one prefill wavefront serves (16-column groups)
+#ifndef PA_PREFILL_GROUPS
+#define PA_PREFILL_GROUPS 2
+#endif
+constexpr int kPrefillGroups = PA_PREFILL_GROUPS;
+constexpr int kPrefillColumns = 16 * kPrefillGroups;
 hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int num_pairs,
                               int num_blocks, int64_t block_bytes, hipStream_t stream);
 hipError_t launch_cache_write(const void *k, const void *v, void *k_cache, void *v_cache,

@@ -23,7 +23,11 @@ namespace pa {
 
 constexpr int kPrefillCols = kPrefillColumns;
 
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2)))
+#ifndef PA_PREFILL_WAVES_PER_EU
+#define PA_PREFILL_WAVES_PER_EU 2
+#endif
+
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
 void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ tables,
                          const int32_t *__restrict__ cu_q, const int32_t *__restrict__ ctx_lens,
                          void *__restrict__ out) {
@@ -48,12 +52,12 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
     if (kmax <= 0) return;
 
     // this lane's columns: column cg * 16 + row16 = head hj of chunk row r
-    int ncol[2], rowid[2], head[2];
-    bool ok[2];
-    bf16x8 qv[2][4];
-    Acc a[2];
+    int ncol[kPrefillGroups], rowid[kPrefillGroups], head[kPrefillGroups];
+    bool ok[kPrefillGroups];
+    bf16x8 qv[kPrefillGroups][4];
+    Acc a[kPrefillGroups];
 #pragma unroll
-    for (int cg = 0; cg < 2; cg++) {
+    for (int cg = 0; cg < kPrefillGroups; cg++) {
         const int col = cg * 16 + ln.row16;
         const int r = r0 + col / G;
         head[cg] = g * G + col % G;
@@ -104,14 +108,14 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the wait
             if ((unsigned)phys[j] < (unsigned)p.num_blocks) {
 #pragma unroll
-                for (int cg = 0; cg < 2; cg++)
+                for (int cg = 0; cg < kPrefillGroups; cg++)
                     tile_update<true>(kr[j], vr[j], qv[cg], ncol[cg] - t * kTile, p.scale_log2,
                                       a[cg], ln);
             }
         }
     }
 #pragma unroll
-    for (int cg = 0; cg < 2; cg++) {
+    for (int cg = 0; cg < kPrefillGroups; cg++) {
         acc_finish(a[cg]);
         if (ok[cg])
             store_row((char *)out + ((size_t)rowid[cg] * p.num_q_heads + head[cg]) * kD * 2,
