@@ -414,8 +414,9 @@ void decode_vector_balanced_kernel(const DecodeParams args, const int32_t *__res
 #pragma unroll
             for (int i = 0; i < PASSES; i++) {
                 const int lo = (i * TPW + r) * kRow + c * 16;
-                kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lo, 0, 0));
-                vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lo, 0, 0));
+                // non-temporal: each tile is read once (evict-first lines)
+                kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lo, 0, 2));
+                vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lo, 0, 2));
             }
             return rows;
         };

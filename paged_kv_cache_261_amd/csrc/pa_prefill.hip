@@ -88,7 +88,10 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
         const int rows = in ? min(kTile, kmax - t * kTile) : 0;
         const size_t off = ((((size_t)(in ? phys : 0) * p.num_kv_heads + g) << log2bs) +
                             ((t * kTile) & bs_mask)) * (size_t)kRowBytes;
-        load_tile_rows(kbase, vbase, off, rows, ln, kr, vr);
+        // default cache policy: the wavefronts of one (sequence, KV head)
+        // read the same tiles in turn (with the non-temporal hint the
+        // prefill took 0.61 ms instead of 0.48)
+        load_tile_rows<kReuseAux>(kbase, vbase, off, rows, ln, kr, vr);
     };
     // phys[j]: block id of the tile in buffer j (kept, not re-read, so no
     // table read sits between a tile's compute and the next load)
