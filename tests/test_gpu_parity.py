@@ -331,6 +331,54 @@ def test_balanced_merge_by_boundary(dtype, algo, d):
     H.assert_close_to_oracle(got, ref, dtype, f"boundary merge {dtype} d {d}")
 
 
+def random_decode_case(seed):
+    """One seeded random decode problem: dtype, head dim, group size, block
+    size, batch and context mix (empty, one token, tile and block edges,
+    long), the pool a random permutation with spare blocks."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["f32", "bf16"][int(rng.integers(2))]
+    d = int(rng.choice([16, 32, 64, 128, 256] if dtype == "f32" else [32, 64, 128, 128]))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+    hkv = int(rng.integers(1, 4))
+    bs = int(rng.choice([1, 4, 8, 16, 32, 64]))
+    B = int(rng.integers(1, 12))
+    edge = [0, 1, 15, 16, 17, 31, 32, 33, bs, bs + 1, 511, 512, 513]
+    ctxs = [int(rng.choice(edge)) if rng.random() < 0.5 else int(rng.integers(1, 1500))
+            for _ in range(B)]
+    q = S._normal(rng, (B, hkv * G, d), dtype)
+    kl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    vl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    nb = sum((n + bs - 1) // bs for n in ctxs) + int(rng.integers(1, 20))
+    kc, vc, tab = H.paginate(kl, vl, bs, nb, rng, dtype)
+    return dtype, d, G, bs, q, kc, vc, tab, np.array(ctxs, dtype=np.int32)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_decode_problems(seed):
+    """Seeded random shapes against the oracle in every mode and kernel the
+    shape admits (single pass, fixed partitions, balanced, shared, auto)."""
+    dtype, d, G, bs, q, kc, vc, tab, ctx = random_decode_case(seed)
+    scale = 1 / math.sqrt(d)
+    ref = pao.decode_concat(q, kc, vc, tab, ctx, scale)
+    kd, vd = H.to_dev(kc), H.to_dev(vc)
+    mfma_ok = dtype == "bf16" and d == 128 and bs >= 16 and G <= 16
+    vbal_ok = bs >= 16 and (dtype == "f32" or d >= 32)
+    runs = [(AUTO, -1), (VECTOR, 0), (VECTOR, max(bs, 64))]
+    if vbal_ok:
+        runs.append((VECTOR, pa.PA_PARTITION_BALANCED))
+    if mfma_ok:
+        runs += [(MFMA, 0), (MFMA, 256), (MFMA, pa.PA_PARTITION_BALANCED),
+                 (MFMA, pa.PA_PARTITION_SHARED)]
+    for algo, part in runs:
+        note(f"[gpu parity] random case {seed}: {dtype} d {d} G {G} bs {bs} B {len(ctx)} "
+             f"algo {algo} partition {part}")
+        got = H.gpu_decode(q, kd, vd, tab, ctx, scale, None, part, algo)
+        for b, n in enumerate(ctx):
+            if n == 0:
+                assert (got[b] == 0).all()
+        H.assert_close_to_oracle(got, ref, dtype, f"random case {seed} algo {algo} part {part}")
+
+
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 16])
 def test_group_sizes_mfma(G):
     rng = np.random.default_rng(G)
