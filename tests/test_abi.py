@@ -191,3 +191,21 @@ def prefill_call(lib, **kw):
 ])
 def test_prefill_rejects_bad_arguments(lib, kw, status):
     assert prefill_call(lib, **kw) == status
+
+
+def test_binding_has_no_cpu_fallback(lib, monkeypatch):
+    """The Python binding computes nothing itself: host tensors are refused
+    before any call, and a missing library is an import error."""
+    import torch
+    from paged_kv_cache_261_amd import pa
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    kc = torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16)
+    tab = torch.zeros(2, 1, dtype=torch.int32)
+    ctx = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pa.pa_decode(torch.empty_like(q), q, kc, kc, tab, ctx, 0.1, 1, 0, None)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pa.pa_reshape_and_cache(q[:, :2], q[:, :2], kc, kc, torch.zeros(2, dtype=torch.int64))
+    monkeypatch.setattr(pa, "LIB_PATH", "/nonexistent/libpa.so")
+    with pytest.raises(ImportError):
+        pa._load()
