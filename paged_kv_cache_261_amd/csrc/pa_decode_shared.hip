@@ -379,25 +379,31 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
 // ---------------------------------------------------------------------------
 // One workgroup of 4 wavefronts per (KV head, pack) unit.  The unit's
 // pieces -- the partial slots whose directory entry names it, among the
-// wavefronts whose shares overlap the unit -- are listed once in LDS in
-// ascending order; then all 32 columns are merged at once, 8 threads per
-// column and 16 dims per thread, pieces summed in list order.
+// wavefronts whose shares overlap the unit -- are listed in ascending order;
+// then all 32 columns are merged at once, 8 threads per column and 16 dims
+// per thread, pieces summed in list order.  Every wavefront finds the
+// unit's position and lists the pieces itself (into its own LDS region), so
+// the workgroup needs no barrier; up to kDirect pieces are loaded in one
+// round and merged in registers.
 constexpr int kReduceThreads = 256;
+constexpr int kReduceWaves = kReduceThreads / kWave;
+constexpr int kDirect = 6;
 
 template <int NPK, int NCG>
 __global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
     const SharedParams p, const int *__restrict__ ws_dir, const int *__restrict__ ws_cost) {
-    extern __shared__ int lds[];                   // red[4] | count | pieces[2 W]
-    int *red = lds, *count = lds + 4, *pieces = lds + 8;
+    extern __shared__ int lds[];                   // pieces[kReduceWaves][2 W]
     const int unit = blockIdx.x;                   // g * NPACK + k
     const int NPACK = p.num_packs;
     const int k = unit % NPACK, g = unit / NPACK;
     const int G = p.group;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    int *pieces = lds + wave * 2 * p.num_waves;
 
     // position of the unit in the item stream (as the decode kernel split it)
+    const int U = __builtin_amdgcn_readfirstlane(ws_cost[k]);
     int before = 0, all = 0;
-    for (int kk = tid; kk < NPACK; kk += kReduceThreads) {
+    for (int kk = lane; kk < NPACK; kk += kWave) {
         const int u = ws_cost[kk];
         all += u;
         if (kk < k) before += u;
@@ -407,15 +413,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
         before += __shfl_xor(before, o);
         all += __shfl_xor(all, o);
     }
-    if (lane == 0) {
-        red[wave] = before;
-        pieces[wave] = all;   // scratch until the list is built
-    }
-    __syncthreads();
-    const int S = red[0] + red[1] + red[2] + red[3];
-    const int TT = pieces[0] + pieces[1] + pieces[2] + pieces[3];
-    const int U = ws_cost[k];
-    __syncthreads();
+    const int S = before, TT = all;
     int first = 0, last = -1;
     if (U > 0) {
         const int C = (TT * p.num_kv_heads + p.num_waves - 1) / p.num_waves;
@@ -423,19 +421,14 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
         first = start / C;
         last = (start + U - 1) / C;
     }
-    if (wave == 0) {
-        int n = 0;
-        for (int e0 = 2 * first; e0 < 2 * last + 2; e0 += kWave) {
-            const int e = e0 + lane;
-            const bool hit = e < 2 * last + 2 && ws_dir[e] == unit;
-            const unsigned long long m = __ballot(hit);
-            if (hit) pieces[n + __builtin_popcountll(m & ((1ull << lane) - 1))] = e;
-            n += __builtin_popcountll(m);
-        }
-        if (lane == 0) *count = n;
+    int npieces = 0;
+    for (int e0 = 2 * first; e0 < 2 * last + 2; e0 += kWave) {
+        const int e = e0 + lane;
+        const bool hit = e < 2 * last + 2 && ws_dir[e] == unit;
+        const unsigned long long m = __ballot(hit);
+        if (hit) pieces[npieces + __builtin_popcountll(m & ((1ull << lane) - 1))] = e;
+        npieces += __builtin_popcountll(m);
     }
-    __syncthreads();
-    const int npieces = *count;
 
     // 8 lanes per column, 16 dims per lane: the 32 columns at once
     const int c = tid / 8, sub = tid % 8;
@@ -450,25 +443,62 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
         return;
     }
     if (npieces == 0) return;                       // finished by one wavefront
-    float M = -INFINITY;
-    for (int q = 0; q < npieces; q++) M = fmaxf(M, p.ws_m[(size_t)pieces[q] * kMaxCols + c]);
     float num[16], den = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; e++) num[e] = 0.f;
-    if (M != -INFINITY) {
-        for (int q = 0; q < npieces; q++) {
-            const size_t prow = (size_t)pieces[q] * kMaxCols + c;
-            const float mq = p.ws_m[prow];
-            const float wq = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - M);
-            den = fmaf(wq, p.ws_l[prow], den);
-            const float4 *src = (const float4 *)(p.ws_acc + prow * kD + 16 * sub);
+    if (npieces <= kDirect) {
+        // every piece's m, l and 16 accumulator values in one round of loads
+        float mq[kDirect], lq[kDirect];
+        float4 aq[kDirect][4];
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const float4 a4 = src[v];
-                num[4 * v + 0] = fmaf(wq, a4.x, num[4 * v + 0]);
-                num[4 * v + 1] = fmaf(wq, a4.y, num[4 * v + 1]);
-                num[4 * v + 2] = fmaf(wq, a4.z, num[4 * v + 2]);
-                num[4 * v + 3] = fmaf(wq, a4.w, num[4 * v + 3]);
+        for (int q = 0; q < kDirect; q++) {
+            if (q < npieces) {
+                const size_t prow = (size_t)pieces[q] * kMaxCols + c;
+                mq[q] = p.ws_m[prow];
+                lq[q] = p.ws_l[prow];
+                const float4 *src = (const float4 *)(p.ws_acc + prow * kD + 16 * sub);
+#pragma unroll
+                for (int v = 0; v < 4; v++) aq[q][v] = src[v];
+            }
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kDirect; q++)
+            if (q < npieces) M = fmaxf(M, mq[q]);
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int q = 0; q < kDirect; q++) {
+                if (q < npieces && mq[q] != -INFINITY) {   // empty piece: weight 0
+                    const float wq = __builtin_amdgcn_exp2f(mq[q] - M);
+                    den = fmaf(wq, lq[q], den);
+#pragma unroll
+                    for (int v = 0; v < 4; v++) {
+                        num[4 * v + 0] = fmaf(wq, aq[q][v].x, num[4 * v + 0]);
+                        num[4 * v + 1] = fmaf(wq, aq[q][v].y, num[4 * v + 1]);
+                        num[4 * v + 2] = fmaf(wq, aq[q][v].z, num[4 * v + 2]);
+                        num[4 * v + 3] = fmaf(wq, aq[q][v].w, num[4 * v + 3]);
+                    }
+                }
+            }
+        }
+    } else {
+        float M = -INFINITY;
+        for (int q = 0; q < npieces; q++) M = fmaxf(M, p.ws_m[(size_t)pieces[q] * kMaxCols + c]);
+        if (M != -INFINITY) {
+            for (int q = 0; q < npieces; q++) {
+                const size_t prow = (size_t)pieces[q] * kMaxCols + c;
+                const float mq = p.ws_m[prow];
+                const float wq = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - M);
+                den = fmaf(wq, p.ws_l[prow], den);
+                const float4 *src = (const float4 *)(p.ws_acc + prow * kD + 16 * sub);
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    const float4 a4 = src[v];
+                    num[4 * v + 0] = fmaf(wq, a4.x, num[4 * v + 0]);
+                    num[4 * v + 1] = fmaf(wq, a4.y, num[4 * v + 1]);
+                    num[4 * v + 2] = fmaf(wq, a4.z, num[4 * v + 2]);
+                    num[4 * v + 3] = fmaf(wq, a4.w, num[4 * v + 3]);
+                }
             }
         }
     }
@@ -498,8 +528,8 @@ static hipError_t launch_shared_t(const SharedParams &p, int phase, hipStream_t 
     if (phase & 2)
         hipLaunchKernelGGL((reduce_shared_kernel<NPK, NCG>),
                            dim3((unsigned)p.num_kv_heads * p.num_packs), dim3(kReduceThreads),
-                           (8 + 2 * (size_t)p.num_waves) * sizeof(int), stream, p, p.ws_dir,
-                           p.ws_cost);
+                           (size_t)kReduceWaves * 2 * p.num_waves * sizeof(int), stream, p,
+                           p.ws_dir, p.ws_cost);
     return hipGetLastError();
 }
 
