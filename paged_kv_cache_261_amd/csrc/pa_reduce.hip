@@ -97,6 +97,57 @@ __device__ __forceinline__ void merge_row(T *out, int n, const float *m, const f
     store_out(out + i, den > 0.f ? num / den : 0.f);
 }
 
+// The same merge for a row of n <= 64 pieces of which at most kSparse have
+// a non-zero weight (the matrix-core split merges a wavefront's consecutive
+// partitions itself and marks the others empty): every wavefront takes one
+// piece per lane for the weights (no LDS, no barrier), then the non-empty
+// pieces' accumulators are read in one round.  Returns false, having done
+// nothing, when the row does not qualify.
+constexpr int kSparse = 16;
+
+template <typename T, int D>
+__device__ __forceinline__ bool merge_row_sparse(T *out, int n, const float *m, const float *l,
+                                                 const float *acc, size_t as) {
+    constexpr int kW = D < kWave ? D : kWave;
+    if (n > kW) return false;
+    const int lane = threadIdx.x % kW;
+    const float mq = lane < n ? m[lane] : -INFINITY;
+    const float lq = lane < n ? l[lane] : 0.f;   // loaded beside m: one round trip
+    float M = mq;
+#pragma unroll
+    for (int o = kW / 2; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kW));
+    const float wq = (mq == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mq - M);
+    float dl = wq * lq;
+#pragma unroll
+    for (int o = kW / 2; o >= 1; o >>= 1) dl += __shfl_xor(dl, o, kW);
+    unsigned long long nz = __ballot(wq != 0.f);
+    if (__builtin_popcountll(nz) > kSparse) return false;
+    // pieces in ascending order, as merge_row sums them, kChunk at a time
+    // with all of a chunk's loads issued together; a slot past the last
+    // non-empty piece re-reads the first one (written, so finite) with
+    // weight 0, which leaves the sum unchanged
+    constexpr int kChunk = 8;
+    const int i = threadIdx.x;
+    const int q_first = nz != 0 ? __builtin_ctzll(nz) : 0;
+    float num = 0.f;
+#pragma unroll 1
+    for (int c = 0; c < kSparse && nz != 0; c += kChunk) {
+        float w[kChunk], a[kChunk];
+#pragma unroll
+        for (int r = 0; r < kChunk; r++) {
+            const bool has = nz != 0;
+            const int q = has ? __builtin_ctzll(nz) : q_first;
+            nz &= nz - 1;
+            w[r] = has ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), q)) : 0.f;
+            a[r] = acc[(size_t)q * as + i];
+        }
+#pragma unroll
+        for (int r = 0; r < kChunk; r++) num = fmaf(w[r], a[r], num);
+    }
+    store_out(out + i, dl > 0.f ? num / dl : 0.f);
+    return true;
+}
+
 // Fixed partitions: row = (b, h); piece q is partition q of the row.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void reduce_kernel(const ReduceParams p) {
@@ -107,8 +158,11 @@ __global__ __launch_bounds__(D) void reduce_kernel(const ReduceParams p) {
     const int n_parts = (n + p.partition_size - 1) / p.partition_size;
     if (n_parts <= 1) return;                   // phase 1 wrote the output itself
     const size_t prow = (size_t)row * p.num_partitions;
-    merge_row<T, D>((T *)p.out + (size_t)row * D, n_parts, p.ws_m + prow, p.ws_l + prow, 1,
-                    p.ws_acc + prow * D, D, lds + 8, lds);
+    T *out = (T *)p.out + (size_t)row * D;
+    if (merge_row_sparse<T, D>(out, n_parts, p.ws_m + prow, p.ws_l + prow, p.ws_acc + prow * D, D))
+        return;
+    merge_row<T, D>(out, n_parts, p.ws_m + prow, p.ws_l + prow, 1, p.ws_acc + prow * D, D,
+                    lds + 8, lds);
 }
 
 // Units cut into at most this many pieces are merged in registers.
