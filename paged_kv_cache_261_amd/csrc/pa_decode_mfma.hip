@@ -209,7 +209,7 @@ void decode_mfma_balanced_kernel(const DecodeParams args, const int32_t *__restr
     const int lane = threadIdx.x;
     const Lane ln{lane & 15, lane >> 4};
     const int W = p.num_units;
-    const int w = xcd_remap(blockIdx.x, W);
+    const int w = blockIdx.x;       // launch order: see xcd_remap
     const int B = p.num_seqs;
     const int PT = p.partition_size / kTile;   // tiles per partition; 0: free cuts
 

@@ -145,7 +145,7 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
     const int lane = threadIdx.x;
     const Lane ln{lane & 15, lane >> 4};
     const int W = p.num_waves;
-    const int w = xcd_remap(blockIdx.x, W);
+    const int w = blockIdx.x;       // launch order: see xcd_remap
     const int G = p.group;
     const int NPACK = p.num_packs;
 

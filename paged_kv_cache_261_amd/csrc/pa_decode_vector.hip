@@ -316,7 +316,7 @@ void decode_vector_balanced_kernel(const DecodeParams args, const int32_t *__res
     const int r = lane / LPT;                  // token slot within a pass
     const int c = lane % LPT;                  // 16-byte chunk of head_dim
     const int W = p.num_units;
-    const int w = xcd_remap(blockIdx.x, W);
+    const int w = blockIdx.x;       // launch order: see xcd_remap
     const int B = p.num_seqs;
     const int G = p.group;
 

@@ -118,6 +118,12 @@ constexpr int kMaxCols = 32;
 // the same time.  Units are numbered with the sequence fastest, so the
 // samples of one prompt (adjacent sequences sharing prefix blocks) reading
 // the same (KV head, partition) meet in one XCD's L2.
+//
+// The persistent kernels do not remap: their shares of the tile stream (KV
+// head slowest) would then put one KV head's slices of every block on one
+// XCD, and an XCD reading a single head's slices drew unevenly on the HBM
+// channels -- one XCD ran 5% behind the rest and set the kernel's end.  In
+// launch order the eight XCDs take shares from all heads alike.
 __device__ __forceinline__ int xcd_remap(int w, int n) {
     const int q = n / kNumXcd, r = n % kNumXcd;
     const int x = w % kNumXcd, slot = w / kNumXcd;
