@@ -376,7 +376,10 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
     const int rows_per_wave = pa::kPrefillColumns / p.group;
     p.units_per_seq = (max_q_len + rows_per_wave - 1) / rows_per_wave;
     p.scale_log2 = scale * 1.4426950408889634f;
-    if ((int64_t)num_seqs * num_kv_heads * p.units_per_seq > 0x7fffffff) return PA_ERR_SHAPE;
+    // the grid: (sequence, KV head) groups rounded up to whole rounds of XCDs
+    const int64_t groups = (int64_t)num_seqs * num_kv_heads;
+    if ((groups + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd * p.units_per_seq > 0x7fffffff)
+        return PA_ERR_SHAPE;
     const hipError_t e = pa::launch_prefill(p, (hipStream_t)stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

@@ -17,9 +17,36 @@
 // limit is its row's position, so the last tiles are partly masked per
 // column.  Wavefronts of one (sequence, KV head) stream the same K/V tiles
 // close together in time, so the repeats are served by L2.
+//
+// Order of the wavefronts: a unit's work grows with its sequence's context
+// and its rows' positions, and the grid is many times larger than what is
+// resident, so the dispatch order sets the end.  The (sequence, KV head)
+// groups are ranked by context length, longest first, and dealt to the
+// eight XCDs round-robin (group i to XCD i % 8: every XCD gets a share of
+// long and short contexts); within a group the units run from the last
+// rows (most keys) to the first.  All units of a group stay on one XCD and
+// run back to back, which keeps its K/V tiles in that XCD's L2.
 #include "pa_mfma_tile.h"
 
 namespace pa {
+
+// The sequence of rank r when sequences are ordered by context length,
+// longest first (ties by index).  Each lane holds one sequence's length;
+// with more sequences than lanes the order is the plain one.
+__device__ __forceinline__ int seq_of_rank(const PrefillParams &p, const int32_t *ctx_lens,
+                                           int r) {
+    const int B = p.num_seqs;
+    if (B > kWave) return r;
+    const int lane = threadIdx.x;
+    const int key = lane < B ? clamp_ctx(ctx_lens[lane], p.max_context_len) : -1;
+    int rank = 0;
+    for (int m = 0; m < B; m++) {
+        const int km = __builtin_amdgcn_readlane(key, m);
+        rank += (km > key || (km == key && m < lane)) ? 1 : 0;
+    }
+    // the ranks of lanes 0 .. B-1 are a permutation of 0 .. B-1
+    return __builtin_ctzll(__ballot(lane < B && rank == r));
+}
 
 constexpr int kPrefillCols = kPrefillColumns;
 
@@ -36,11 +63,14 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
     const Lane ln{lane & 15, lane >> 4};
     const int G = p.group;
     const int TPU = kPrefillCols / G;                       // chunk rows per wavefront
-    // unit = (u fastest, then KV head g, then sequence b); XCD-aware order
-    const int unit = xcd_remap(blockIdx.x, gridDim.x);
-    const int u = unit % p.units_per_seq;
-    const int g = (unit / p.units_per_seq) % p.num_kv_heads;
-    const int b = unit / (p.units_per_seq * p.num_kv_heads);
+    // workgroup -> (XCD, slot on it) -> group i = (rank, KV head), unit u
+    const int xcd = blockIdx.x % kNumXcd;
+    const int slot = blockIdx.x / kNumXcd;
+    const int i = (slot / p.units_per_seq) * kNumXcd + xcd;
+    if (i >= p.num_seqs * p.num_kv_heads) return;
+    const int u = p.units_per_seq - 1 - slot % p.units_per_seq;
+    const int g = i % p.num_kv_heads;
+    const int b = __builtin_amdgcn_readfirstlane(seq_of_rank(p, ctx_lens, i / p.num_kv_heads));
     const int q0 = __builtin_amdgcn_readfirstlane(cu_q[b]);
     const int nq = __builtin_amdgcn_readfirstlane(cu_q[b + 1]) - q0;
     const int r0 = u * TPU;                                 // first chunk row of the unit
@@ -127,7 +157,10 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
 }
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
-    const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads * p.units_per_seq;
+    // groups dealt to the XCDs round-robin: kNumXcd * ceil(groups / kNumXcd)
+    // slots of units_per_seq workgroups (the surplus ones return at once)
+    const int64_t groups = (int64_t)p.num_seqs * p.num_kv_heads;
+    const int64_t units = (groups + kNumXcd - 1) / kNumXcd * kNumXcd * p.units_per_seq;
     if (units == 0) return hipSuccess;
     hipLaunchKernelGGL(prefill_mfma_kernel, dim3((unsigned)units), dim3(kWave), 0, stream, p,
                        p.block_tables, p.cu_seqlens_q, p.context_lens, p.out);
