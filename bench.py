@@ -43,9 +43,13 @@ METRIC = "paged decode attention: achieved KV-read GB/s (% HBM peak) and tokens/
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 DEFAULT_CONFIG = "gqa_bf16"
+# Sources of the decode launch (slot write, decode kernels, merges and the
+# host code that plans them): HBM byte counters stored for a decode workload
+# stay valid while these hash the same.  The copy-on-write and prefill kernels
+# are separate launches and do not take part.
 KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_shared.hip", "pa_decode_vector.hip",
                   "pa_reduce.hip", "pa_cache_write.hip", "pa_api.cpp", "pa_internal.h",
-                  "pa_mfma_tile.h", "pa_copy_blocks.hip", "pa_prefill.hip"]
+                  "pa_mfma_tile.h"]
 
 
 def log(msg):
