@@ -101,6 +101,12 @@ def to_host(t):
     return t.cpu().numpy()
 
 
+def as_bits(t):
+    """A device tensor viewed as integers of its element width (exact compares, NaN included)."""
+    import torch
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
 def dev_empty_pool(cfg, poison=True, device="cuda"):
     import torch
     shape = (cfg.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim)

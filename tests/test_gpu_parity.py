@@ -448,6 +448,80 @@ def test_physical_placement_and_repeats_do_not_change_bits(dtype, algo):
         np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pool_beyond_4gib(dtype):
+    """A pool of 6 GiB per cache, with the sequences' blocks placed where
+    their byte offsets cross 2^31, cross 2^32 and sit at the very top: the
+    slot write, decode in every mode and kernel the shape admits,
+    copy-on-write and prefill give the bits they give for the same logical
+    content at low block ids, and the low placement matches the oracle."""
+    rng = np.random.default_rng(77)
+    hkv, d = 8, (128 if dtype == "bf16" else 64)
+    G = 4 if dtype == "bf16" else 1
+    hq, bs = hkv * G, 16
+    esz = 2 if dtype == "bf16" else 4
+    block_bytes = hkv * bs * d * esz                       # 32 KiB either way
+    nb_big = (6 << 30) // block_bytes
+    ctxs = [1, 300, 2500, 4097]
+    need = sum((n + bs - 1) // bs for n in ctxs)
+    nb_small = need + 8
+    scale = 1 / math.sqrt(d)
+    q = S._normal(rng, (len(ctxs), hq, d), dtype)
+    kl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    vl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    kc, vc, tab = H.paginate(kl, vl, bs, nb_small, rng, dtype)
+    ctx = np.array(ctxs, dtype=np.int32)
+    ref = pao.decode_concat(q, kc, vc, tab, ctx, scale)
+    kd_s, vd_s = H.to_dev(kc), H.to_dev(vc)
+    modes = [(MFMA, 0), (MFMA, 512), (MFMA, -2), (MFMA, -3)] if dtype == "bf16" else []
+    modes += [(VECTOR, 0), (VECTOR, 512), (VECTOR, -2)]
+    low = {m: H.gpu_decode(q, kd_s, vd_s, tab, ctx, scale, None, m[1], m[0]) for m in modes}
+    for m, got in low.items():
+        H.assert_close_to_oracle(got, ref, dtype, f"low placement, mode {m}")
+    chunks = [1, 40, 100, 7]
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    qp = S._normal(rng, (int(cu[-1]), hq, d), dtype)
+    if dtype == "bf16":
+        pf_low = gpu_prefill(qp, kd_s, vd_s, tab, cu, ctx, scale)
+        H.assert_close_to_oracle(pf_low, pao.prefill_concat(qp, kc, vc, tab, cu, ctx, scale),
+                                 dtype, "low placement, prefill")
+    # every token of every sequence, for the slot write
+    k_all = np.concatenate(kl)
+    v_all = np.concatenate(vl)
+    cfg = S.Config(name="big", seed=0, num_seqs=len(ctxs), num_q_heads=hq, num_kv_heads=hkv,
+                   head_dim=d, block_size=bs, num_blocks=nb_big,
+                   max_blocks_per_seq=tab.shape[1], dtype=dtype, scale=scale, description="")
+    kd, vd = H.dev_empty_pool(cfg)
+    bases = [(1 << 31) // block_bytes - nb_small // 2, (1 << 32) // block_bytes - nb_small // 2,
+             nb_big - nb_small]
+    for base in bases:
+        note(f"pool beyond 4 GiB: {dtype}, blocks {base}..{base + nb_small - 1} of {nb_big}")
+        tab_big = np.where(tab >= 0, tab + base, -1).astype(np.int32)
+        slots = np.concatenate([tab_big[b, np.arange(n) // bs].astype(np.int64) * bs +
+                                np.arange(n) % bs for b, n in enumerate(ctxs)])
+        H.dev_write(kd, vd, k_all, v_all, slots)
+        torch.cuda.synchronize()
+        assert torch.equal(H.as_bits(kd[base:base + nb_small]), H.as_bits(kd_s))
+        assert torch.equal(H.as_bits(vd[base:base + nb_small]), H.as_bits(vd_s))
+        for m in modes:
+            got = H.gpu_decode(q, kd, vd, tab_big, ctx, scale, None, m[1], m[0])
+            np.testing.assert_array_equal(got, low[m], err_msg=f"base {base}, mode {m}")
+        if dtype == "bf16":
+            np.testing.assert_array_equal(gpu_prefill(qp, kd, vd, tab_big, cu, ctx, scale),
+                                          pf_low, err_msg=f"base {base}, prefill")
+    # copy-on-write between blocks past 4 GiB: the longest sequence's first
+    # blocks to the blocks just below the top placement
+    src = tab_big[3, :6]
+    dst = np.arange(bases[-1] - 1, bases[-1] - 7, -1, dtype=np.int32)
+    pa.pa_copy_blocks(kd, vd, H.to_dev(np.stack([src, dst], axis=1).astype(np.int32)))
+    torch.cuda.synchronize()
+    for sblk, dblk in zip(src, dst):
+        assert torch.equal(H.as_bits(kd[int(dblk)]), H.as_bits(kd[int(sblk)]))
+        assert torch.equal(H.as_bits(vd[int(dblk)]), H.as_bits(vd[int(sblk)]))
+    del kd, vd
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("part", [512, -2, -3])
 def test_phases_equal_one_call(part):
     w, kd, vd, kh, vh = full("long_split_bf16")
