@@ -12,20 +12,21 @@
 // How (matrix cores; bf16, head_dim 128, block_size >= 16, group size
 // G <= 16): one wavefront serves 32 query-head columns of one KV head -- the
 // G heads of TPU = 32 / G consecutive chunk rows (two 16-column groups that
-// share every K/V load) -- and walks the keys 0 .. (its last row's position)
+// share every K/V tile) -- and walks the keys 0 .. (the last row's position)
 // in 16-token tiles with the tile step of pa_mfma_tile.h; a column's causal
 // limit is its row's position, so the last tiles are partly masked per
-// column.  Wavefronts of one (sequence, KV head) stream the same K/V tiles
-// close together in time, so the repeats are served by L2.
+// column.  A workgroup of kWgWaves such wavefronts (consecutive units of one
+// (sequence, KV head)) reads each K/V tile from memory once and shares it
+// through LDS.
 //
-// Order of the wavefronts: a unit's work grows with its sequence's context
+// Order of the workgroups: a unit's work grows with its sequence's context
 // and its rows' positions, and the grid is many times larger than what is
 // resident, so the dispatch order sets the end.  The (sequence, KV head)
 // groups are ranked by context length, longest first, and dealt to the
 // eight XCDs round-robin (group i to XCD i % 8: every XCD gets a share of
-// long and short contexts); within a group the units run from the last
-// rows (most keys) to the first.  All units of a group stay on one XCD and
-// run back to back, which keeps its K/V tiles in that XCD's L2.
+// long and short contexts); within a group the unit blocks run from the
+// last rows (most keys) to the first.  All blocks of a group stay on one XCD
+// and run back to back, which keeps its K/V tiles in that XCD's L2.
 #include "pa_mfma_tile.h"
 
 namespace pa {
@@ -37,7 +38,7 @@ __device__ __forceinline__ int seq_of_rank(const PrefillParams &p, const int32_t
                                            int r) {
     const int B = p.num_seqs;
     if (B > kWave) return r;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
     const int key = lane < B ? clamp_ctx(ctx_lens[lane], p.max_context_len) : -1;
     int rank = 0;
     for (int m = 0; m < B; m++) {
@@ -54,34 +55,70 @@ constexpr int kPrefillCols = kPrefillColumns;
 #define PA_PREFILL_WAVES_PER_EU 2
 #endif
 
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
-void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ tables,
+// ---------------------------------------------------------------------------
+// Each tile (16 rows of K and of V, 8 KiB) is read from memory once per
+// workgroup in 16-byte pieces, so every request covers whole 128-byte
+// lines; the wavefronts then read the tile out of LDS in exactly the
+// register layout of the tile step, so the arithmetic -- and every output
+// bit -- is that of a wavefront loading the tile itself.  LDS rows are
+// padded to 272 bytes: the 16 lanes that read one column of 16 K rows then
+// hit 16 different bank groups.  Two stages alternate: while tile t is read
+// and computed, tile t+1 (loaded one iteration earlier) is written into the
+// other stage and tile t+2 is loaded; one LDS-only barrier per tile (no
+// wait on the loads in flight).
+// ---------------------------------------------------------------------------
+#ifndef PA_PREFILL_WG_WAVES
+#define PA_PREFILL_WG_WAVES 4
+#endif
+constexpr int kWgWaves = PA_PREFILL_WG_WAVES;
+constexpr int kWgThreads = kWave * kWgWaves;
+// 16-byte pieces of one tile: 256 of K, then 256 of V
+constexpr int kPieces = 2 * kTile * kRowBytes / 16;
+static_assert(kPieces % kWgThreads == 0, "tile pieces must divide over the workgroup");
+constexpr int kPiecesPerThread = kPieces / kWgThreads;
+constexpr int kLdsRow = kRowBytes + 16;
+constexpr int kStage = 2 * kTile * kLdsRow;   // K rows, then V rows
+
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__global__ __launch_bounds__(kWgThreads)
+__attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
+void prefill_wg_kernel(const PrefillParams args, const int32_t *__restrict__ tables,
                          const int32_t *__restrict__ cu_q, const int32_t *__restrict__ ctx_lens,
                          void *__restrict__ out) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
     const PrefillParams &p = args;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Lane ln{lane & 15, lane >> 4};
     const int G = p.group;
-    const int TPU = kPrefillCols / G;                       // chunk rows per wavefront
-    // workgroup -> (XCD, slot on it) -> group i = (rank, KV head), unit u
+    const int TPU = kPrefillCols / G;
+    const int ubs = (p.units_per_seq + kWgWaves - 1) / kWgWaves;   // unit blocks per group
+    // workgroup -> (XCD, slot on it) -> group i = (rank, KV head), unit block
     const int xcd = blockIdx.x % kNumXcd;
     const int slot = blockIdx.x / kNumXcd;
-    const int i = (slot / p.units_per_seq) * kNumXcd + xcd;
-    if (i >= p.num_seqs * p.num_kv_heads) return;
-    const int u = p.units_per_seq - 1 - slot % p.units_per_seq;
+    const int i = (slot / ubs) * kNumXcd + xcd;
+    if (i >= p.num_seqs * p.num_kv_heads) return;             // whole workgroup
+    const int ub = ubs - 1 - slot % ubs;
     const int g = i % p.num_kv_heads;
     const int b = __builtin_amdgcn_readfirstlane(seq_of_rank(p, ctx_lens, i / p.num_kv_heads));
     const int q0 = __builtin_amdgcn_readfirstlane(cu_q[b]);
     const int nq = __builtin_amdgcn_readfirstlane(cu_q[b + 1]) - q0;
-    const int r0 = u * TPU;                                 // first chunk row of the unit
-    if (r0 >= nq) return;
+    const int wg_r0 = ub * kWgWaves * TPU;                    // first chunk row of the block
+    if (wg_r0 >= nq) return;                                  // whole workgroup
     const int n = __builtin_amdgcn_readfirstlane(clamp_ctx(ctx_lens[b], p.max_context_len));
-    const int first_pos = n - nq;                           // position of chunk row 0
-    const int r_end = min(nq, r0 + TPU);
-    const int kmax = first_pos + r_end;                     // keys 0 .. kmax-1
-    if (kmax <= 0) return;
+    const int first_pos = n - nq;
+    const int wg_r_end = min(nq, wg_r0 + kWgWaves * TPU);
+    const int kmax = first_pos + wg_r_end;                    // keys 0 .. kmax-1 for the block
+    if (kmax <= 0) return;                                    // whole workgroup
+    const int r0 = wg_r0 + wave * TPU;                        // this wavefront's first row
+    const int r_end = min(nq, r0 + TPU);                      // r_end <= r0: no rows
 
-    // this lane's columns: column cg * 16 + row16 = head hj of chunk row r
     int ncol[kPrefillGroups], rowid[kPrefillGroups], head[kPrefillGroups];
     bool ok[kPrefillGroups];
     bf16x8 qv[kPrefillGroups][4];
@@ -93,7 +130,7 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
         head[cg] = g * G + col % G;
         ok[cg] = col / G < TPU && r < r_end;
         rowid[cg] = q0 + r;
-        ncol[cg] = ok[cg] ? first_pos + r + 1 : 0;           // keys 0 .. its position
+        ncol[cg] = ok[cg] ? first_pos + r + 1 : 0;
         const char *qrow = (const char *)p.q +
                            (((size_t)(ok[cg] ? rowid[cg] : q0) * p.num_q_heads +
                              (ok[cg] ? head[cg] : 0)) * kD + 8 * ln.grp) * 2;
@@ -113,39 +150,70 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
     const int bs_mask = (1 << log2bs) - 1;
     const int ntiles = (kmax + kTile - 1) / kTile;
     auto phys_of = [&](int t) -> int { return table[(min(t, ntiles - 1) * kTile) >> log2bs]; };
-    auto issue = [&](int t, int phys, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+    // thread tid moves pieces tid, tid + kWgThreads, ...: piece c is bytes
+    // 16 (c % 16) .. of row (c / 16) % 16 of K (c < 256) or of V
+    auto issue = [&](int t, int phys, u32x4 (&gr)[kPiecesPerThread]) {
         const bool in = t < ntiles && (unsigned)phys < (unsigned)p.num_blocks;
         const int rows = in ? min(kTile, kmax - t * kTile) : 0;
         const size_t off = ((((size_t)(in ? phys : 0) * p.num_kv_heads + g) << log2bs) +
                             ((t * kTile) & bs_mask)) * (size_t)kRowBytes;
-        // default cache policy: the wavefronts of one (sequence, KV head)
-        // read the same tiles in turn (with the non-temporal hint the
-        // prefill took 0.61 ms instead of 0.48)
-        load_tile_rows<kReuseAux>(kbase, vbase, off, rows, ln, kr, vr);
-    };
-    // phys[j]: block id of the tile in buffer j (kept, not re-read, so no
-    // table read sits between a tile's compute and the next load)
-    u32x4 kr[2][4], vr[2][4];
-    int phys[2];
-    phys[0] = phys_of(0);
-    issue(0, phys[0], kr[0], vr[0]);
-    int phys_next = phys_of(1);
-    for (int t0 = 0; t0 < ntiles; t0 += 2) {
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(kbase + off), (short)0, rows * kRowBytes, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(vbase + off), (short)0, rows * kRowBytes, kRsrcWord3);
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int t = t0 + j;
-            if (t >= ntiles) break;
-            phys[j ^ 1] = phys_next;
-            issue(t + 1, phys_next, kr[j ^ 1], vr[j ^ 1]);
-            phys_next = phys_of(t + 2);
-            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the wait
-            if ((unsigned)phys[j] < (unsigned)p.num_blocks) {
-#pragma unroll
-                for (int cg = 0; cg < kPrefillGroups; cg++)
-                    tile_update<true>(kr[j], vr[j], qv[cg], ncol[cg] - t * kTile, p.scale_log2,
-                                      a[cg], ln);
-            }
+        for (int j = 0; j < kPiecesPerThread; j++) {
+            const int c = tid + j * kWgThreads;
+            const int goff = ((c >> 4) & (kTile - 1)) * kRowBytes + (c & 15) * 16;
+            // K or V is the same for the whole wavefront (256 is a multiple of 64)
+            const bool of_k = wave * kWave + j * kWgThreads < kPieces / 2;
+            gr[j] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(of_k ? krs : vrs, goff, 0, kReuseAux));
         }
+    };
+    auto stage_write = [&](int st, const u32x4 (&gr)[kPiecesPerThread]) {
+        char *base = lds + st * kStage;
+#pragma unroll
+        for (int j = 0; j < kPiecesPerThread; j++) {
+            const int c = tid + j * kWgThreads;
+            *(u32x4 *)(base + (c >> 4) * kLdsRow + (c & 15) * 16) = gr[j];
+        }
+    };
+    // the tile step's operands out of a stage (the layout load_tile_rows gives)
+    auto stage_read = [&](int st, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+        const char *base = lds + st * kStage;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            kr[j] = *(const u32x4 *)(base + ln.row16 * kLdsRow + ln.grp * 16 + 64 * j);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            vr[j] = *(const u32x4 *)(base + kTile * kLdsRow + (4 * ln.grp + j) * kLdsRow +
+                                     ln.row16 * 16);
+    };
+
+    u32x4 gr[kPiecesPerThread];
+    int phys_cur = phys_of(0);
+    issue(0, phys_cur, gr);
+    stage_write(0, gr);
+    int phys_n1 = phys_of(1);
+    issue(1, phys_n1, gr);
+    int phys_n2 = phys_of(2);
+    lds_barrier();
+    for (int t = 0; t < ntiles; t++) {
+        const int st = t & 1;
+        u32x4 kr[4], vr[4];
+        stage_read(st, kr, vr);
+        if ((unsigned)phys_cur < (unsigned)p.num_blocks) {
+#pragma unroll
+            for (int cg = 0; cg < kPrefillGroups; cg++)
+                tile_update<true>(kr, vr, qv[cg], ncol[cg] - t * kTile, p.scale_log2, a[cg], ln);
+        }
+        if (t + 1 < ntiles) stage_write(st ^ 1, gr);
+        issue(t + 2, phys_n2, gr);
+        phys_cur = phys_n1;
+        phys_n1 = phys_n2;
+        phys_n2 = phys_of(t + 3);
+        lds_barrier();
     }
 #pragma unroll
     for (int cg = 0; cg < kPrefillGroups; cg++) {
@@ -157,14 +225,12 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
 }
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
-    // groups dealt to the XCDs round-robin: kNumXcd * ceil(groups / kNumXcd)
-    // slots of units_per_seq workgroups (the surplus ones return at once)
     const int64_t groups = (int64_t)p.num_seqs * p.num_kv_heads;
-    const int64_t units = (groups + kNumXcd - 1) / kNumXcd * kNumXcd * p.units_per_seq;
-    if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL(prefill_mfma_kernel, dim3((unsigned)units), dim3(kWave), 0, stream, p,
-                       p.block_tables, p.cu_seqlens_q, p.context_lens, p.out);
+    const int64_t ubs = (p.units_per_seq + kWgWaves - 1) / kWgWaves;
+    const int64_t wgs = (groups + kNumXcd - 1) / kNumXcd * kNumXcd * ubs;
+    if (wgs == 0) return hipSuccess;
+    hipLaunchKernelGGL(prefill_wg_kernel, dim3((unsigned)wgs), dim3(kWgThreads), 0,
+                       stream, p, p.block_tables, p.cu_seqlens_q, p.context_lens, p.out);
     return hipGetLastError();
 }
-
 }  // namespace pa
