@@ -162,7 +162,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
 // query-head columns one prefill wavefront serves (16-column groups)
 #ifndef PA_PREFILL_GROUPS
-#define PA_PREFILL_GROUPS 2
+#define PA_PREFILL_GROUPS 1
 #endif
 constexpr int kPrefillGroups = PA_PREFILL_GROUPS;
 constexpr int kPrefillColumns = 16 * kPrefillGroups;

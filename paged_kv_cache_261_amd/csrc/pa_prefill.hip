@@ -10,9 +10,9 @@
 // p = context_lens[b] - n_b + r attends over positions 0..p.
 //
 // How (matrix cores; bf16, head_dim 128, block_size >= 16, group size
-// G <= 16): one wavefront serves 32 query-head columns of one KV head -- the
-// G heads of TPU = 32 / G consecutive chunk rows (two 16-column groups that
-// share every K/V tile) -- and walks the keys 0 .. (the last row's position)
+// G <= 16): one wavefront serves 16 query-head columns of one KV head (16 x
+// kPrefillGroups with the compile-time knob) -- the G heads of TPU = 16 / G
+// consecutive chunk rows -- and walks the keys 0 .. (the last row's position)
 // in 16-token tiles with the tile step of pa_mfma_tile.h; a column's causal
 // limit is its row's position, so the last tiles are partly masked per
 // column.  A workgroup of kWgWaves such wavefronts (consecutive units of one
@@ -52,7 +52,7 @@ __device__ __forceinline__ int seq_of_rank(const PrefillParams &p, const int32_t
 constexpr int kPrefillCols = kPrefillColumns;
 
 #ifndef PA_PREFILL_WAVES_PER_EU
-#define PA_PREFILL_WAVES_PER_EU 2
+#define PA_PREFILL_WAVES_PER_EU 4
 #endif
 
 // ---------------------------------------------------------------------------
@@ -63,9 +63,10 @@ constexpr int kPrefillCols = kPrefillColumns;
 // bit -- is that of a wavefront loading the tile itself.  LDS rows are
 // padded to 272 bytes: the 16 lanes that read one column of 16 K rows then
 // hit 16 different bank groups.  Two stages alternate: while tile t is read
-// and computed, tile t+1 (loaded one iteration earlier) is written into the
-// other stage and tile t+2 is loaded; one LDS-only barrier per tile (no
-// wait on the loads in flight).
+// and computed out of one, tile t+1 is written into the other and tile t+3
+// is loaded (two register sets hold the tiles in flight, so a load has two
+// iterations to arrive); one LDS-only barrier per tile (no wait on the
+// loads in flight).
 // ---------------------------------------------------------------------------
 #ifndef PA_PREFILL_WG_WAVES
 #define PA_PREFILL_WG_WAVES 4
@@ -87,7 +88,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 __global__ __launch_bounds__(kWgThreads)
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
-void prefill_wg_kernel(const PrefillParams args, const int32_t *__restrict__ tables,
+void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ tables,
                          const int32_t *__restrict__ cu_q, const int32_t *__restrict__ ctx_lens,
                          void *__restrict__ out) {
     __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
@@ -191,29 +192,36 @@ void prefill_wg_kernel(const PrefillParams args, const int32_t *__restrict__ tab
                                      ln.row16 * 16);
     };
 
-    u32x4 gr[kPiecesPerThread];
-    int phys_cur = phys_of(0);
-    issue(0, phys_cur, gr);
-    stage_write(0, gr);
-    int phys_n1 = phys_of(1);
-    issue(1, phys_n1, gr);
-    int phys_n2 = phys_of(2);
+    // tile x is loaded into register set x % 2 three iterations ahead and
+    // written to its stage at the end of the iteration before its own
+    u32x4 gr[2][kPiecesPerThread];
+    int ph0 = phys_of(0), ph1 = phys_of(1), ph2 = phys_of(2), ph3 = phys_of(3);
+    issue(0, ph0, gr[0]);
+    stage_write(0, gr[0]);
+    issue(1, ph1, gr[1]);
+    issue(2, ph2, gr[0]);
     lds_barrier();
-    for (int t = 0; t < ntiles; t++) {
-        const int st = t & 1;
-        u32x4 kr[4], vr[4];
-        stage_read(st, kr, vr);
-        if ((unsigned)phys_cur < (unsigned)p.num_blocks) {
+    for (int t0 = 0; t0 < ntiles; t0 += 2) {
 #pragma unroll
-            for (int cg = 0; cg < kPrefillGroups; cg++)
-                tile_update<true>(kr, vr, qv[cg], ncol[cg] - t * kTile, p.scale_log2, a[cg], ln);
+        for (int j = 0; j < 2; j++) {
+            const int t = t0 + j;
+            if (t >= ntiles) break;
+            u32x4 kr[4], vr[4];
+            stage_read(j, kr, vr);
+            if ((unsigned)ph0 < (unsigned)p.num_blocks) {
+#pragma unroll
+                for (int cg = 0; cg < kPrefillGroups; cg++)
+                    tile_update<true>(kr, vr, qv[cg], ncol[cg] - t * kTile, p.scale_log2,
+                                      a[cg], ln);
+            }
+            if (t + 1 < ntiles) stage_write(j ^ 1, gr[j ^ 1]);
+            issue(t + 3, ph3, gr[j ^ 1]);
+            ph0 = ph1;
+            ph1 = ph2;
+            ph2 = ph3;
+            ph3 = phys_of(t + 4);
+            lds_barrier();
         }
-        if (t + 1 < ntiles) stage_write(st ^ 1, gr);
-        issue(t + 2, phys_n2, gr);
-        phys_cur = phys_n1;
-        phys_n1 = phys_n2;
-        phys_n2 = phys_of(t + 3);
-        lds_barrier();
     }
 #pragma unroll
     for (int cg = 0; cg < kPrefillGroups; cg++) {
@@ -229,7 +237,7 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
     const int64_t ubs = (p.units_per_seq + kWgWaves - 1) / kWgWaves;
     const int64_t wgs = (groups + kNumXcd - 1) / kNumXcd * kNumXcd * ubs;
     if (wgs == 0) return hipSuccess;
-    hipLaunchKernelGGL(prefill_wg_kernel, dim3((unsigned)wgs), dim3(kWgThreads), 0,
+    hipLaunchKernelGGL(prefill_mfma_kernel, dim3((unsigned)wgs), dim3(kWgThreads), 0,
                        stream, p, p.block_tables, p.cu_seqlens_q, p.context_lens, p.out);
     return hipGetLastError();
 }
