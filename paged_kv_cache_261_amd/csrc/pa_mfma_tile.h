@@ -10,7 +10,8 @@
 //   scores   S[16 tokens x 16 columns] = K_tile[16 x 128] . Q^T[128 x 16]
 //            4 x v_mfma_f32_16x16x32_bf16;
 //   softmax  online per column in base-2 log domain; the tile max is reduced
-//            across the 4 lane groups with two row-swap permutes;
+//            across the 4 lane groups with two row-swap permutes, and the
+//            reference max lags the running max by at most 8 (lazy rescale);
 //   P.V      O^T[128 x 16] += V_tile^T[128 x 16 tokens] . P^T[16 x 16]
 //            8 x v_mfma_f32_16x16x16_bf16 (P rounded to bfloat16, fp32
 //            accumulation).
@@ -57,6 +58,17 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer descriptor, CDNA
 constexpr int kStreamAux = 2;
 // Tiles read by many wavefronts in turn (prefill) keep the default policy.
 constexpr int kReuseAux = 0;
+
+// Lazy rescale: a column's reference max (the m the exponents are taken
+// against) moves only when a tile's max exceeds it by more than this many
+// log2 units.  Any reference gives the same softmax -- l and the accumulator
+// are both taken against it and the final O / l cancels it -- and a lag of
+// at most 8 keeps every p <= 2^8, far from the fp32 and bf16 ranges.  Once
+// the reference settles, alpha is exactly 1 for every column and the
+// rescale below is skipped.  0 gives the plain running max.
+#ifndef PA_RESCALE_SLACK
+#define PA_RESCALE_SLACK 8
+#endif
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -141,7 +153,11 @@ __device__ __forceinline__ void tile_update(const u32x4 (&kr)[4], const u32x4 (&
 #pragma unroll
     for (int i = 0; i < 4; i++) s[i] = 4 * ln.grp + i < nv ? S[i] * scale_log2 : -INFINITY;
     const float tmax = xor32_max(xor16_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))));
+#if PA_RESCALE_SLACK > 0
+    float m_new = tmax > a.m + (float)PA_RESCALE_SLACK ? tmax : a.m;
+#else
     float m_new = fmaxf(a.m, tmax);
+#endif
     // Without kMaybeEmpty m_new is finite (the tile has a visible row for
     // every column) and alpha is 0 on a column's first tile (m = -inf).
     // With it, a column that has seen nothing keeps m = -inf: shift by 0
