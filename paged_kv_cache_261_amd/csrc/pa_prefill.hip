@@ -61,8 +61,8 @@ constexpr int kPrefillCols = kPrefillColumns;
 // lines; the wavefronts then read the tile out of LDS in exactly the
 // register layout of the tile step, so the arithmetic -- and every output
 // bit -- is that of a wavefront loading the tile itself.  LDS rows are
-// padded to 272 bytes: the 16 lanes that read one column of 16 K rows then
-// hit 16 different bank groups.  Two stages alternate: while tile t is read
+// padded (below), so the 16 lanes that read one column of 16 K rows do not
+// all fall in the same banks.  Two stages alternate: while tile t is read
 // and computed out of one, tile t+1 is written into the other and tile t+3
 // is loaded (two register sets hold the tiles in flight, so a load has two
 // iterations to arrive); one LDS-only barrier per tile (no wait on the
@@ -77,8 +77,19 @@ constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kPieces = 2 * kTile * kRowBytes / 16;
 static_assert(kPieces % kWgThreads == 0, "tile pieces must divide over the workgroup");
 constexpr int kPiecesPerThread = kPieces / kWgThreads;
-constexpr int kLdsRow = kRowBytes + 16;
-constexpr int kStage = 2 * kTile * kLdsRow;   // K rows, then V rows
+// LDS row padding in bytes, measured: 32 for K and V (288-byte rows) ran
+// 1-2% faster than 16 (the unpadded 256-byte stride puts every K row of a
+// column read in the same banks)
+#ifndef PA_PREFILL_KPAD
+#define PA_PREFILL_KPAD 32
+#endif
+#ifndef PA_PREFILL_VPAD
+#define PA_PREFILL_VPAD 32
+#endif
+constexpr int kLdsRowK = kRowBytes + PA_PREFILL_KPAD;   // LDS row strides (padded)
+constexpr int kLdsRowV = kRowBytes + PA_PREFILL_VPAD;
+constexpr int kVBase = kTile * kLdsRowK;                 // V rows follow the K rows
+constexpr int kStage = kVBase + kTile * kLdsRowV;
 
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -177,7 +188,9 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
 #pragma unroll
         for (int j = 0; j < kPiecesPerThread; j++) {
             const int c = tid + j * kWgThreads;
-            *(u32x4 *)(base + (c >> 4) * kLdsRow + (c & 15) * 16) = gr[j];
+            const int row = c >> 4;   // 0..15: K row, 16..31: V row
+            const int lo = row < kTile ? row * kLdsRowK : kVBase + (row - kTile) * kLdsRowV;
+            *(u32x4 *)(base + lo + (c & 15) * 16) = gr[j];
         }
     };
     // the tile step's operands out of a stage (the layout load_tile_rows gives)
@@ -185,11 +198,10 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
         const char *base = lds + st * kStage;
 #pragma unroll
         for (int j = 0; j < 4; j++)
-            kr[j] = *(const u32x4 *)(base + ln.row16 * kLdsRow + ln.grp * 16 + 64 * j);
+            kr[j] = *(const u32x4 *)(base + ln.row16 * kLdsRowK + ln.grp * 16 + 64 * j);
 #pragma unroll
         for (int j = 0; j < 4; j++)
-            vr[j] = *(const u32x4 *)(base + kTile * kLdsRow + (4 * ln.grp + j) * kLdsRow +
-                                     ln.row16 * 16);
+            vr[j] = *(const u32x4 *)(base + kVBase + (4 * ln.grp + j) * kLdsRowV + ln.row16 * 16);
     };
 
     // tile x is loaded into register set x % 2 three iterations ahead and
