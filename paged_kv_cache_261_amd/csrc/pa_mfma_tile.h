@@ -140,10 +140,12 @@ __device__ __forceinline__ void acc_merge(Acc &dst, const Acc &src) {
 // loaded; nv: rows of the tile visible to this lane's column (tokens at or
 // past nv are selected out).  With kMaybeEmpty a column may see no visible
 // row in this tile nor before it; the update then leaves it untouched.
-template <bool kMaybeEmpty>
-__device__ __forceinline__ void tile_update(const u32x4 (&kr)[4], const u32x4 (&vr)[4],
-                                            const bf16x8 (&qv)[4], int nv, float scale_log2,
-                                            Acc &a, Lane ln) {
+// v_op(nn) gives the A operand of P.V product nn (4 bf16: one dim, tokens
+// 4*grp .. 4*grp+3 of the lane's group).
+template <bool kMaybeEmpty, typename VOp>
+__device__ __forceinline__ void tile_update_v(const u32x4 (&kr)[4], VOp &&v_op,
+                                              const bf16x8 (&qv)[4], int nv, float scale_log2,
+                                              Acc &a, Lane ln) {
     f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; kk++)
@@ -181,15 +183,26 @@ __device__ __forceinline__ void tile_update(const u32x4 (&kr)[4], const u32x4 (&
     const s16x4 pb = __builtin_bit_cast(
         s16x4, (uint2){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
 #pragma unroll
-    for (int nn = 0; nn < 8; nn++) {
-        // dim 8*row16 + nn of tokens 4*grp + 0..3: word nn/2 of each row, low
-        // half for even nn, high half for odd nn
-        const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t d0 = __builtin_amdgcn_perm(vr[1][nn >> 1], vr[0][nn >> 1], sel);
-        const uint32_t d1 = __builtin_amdgcn_perm(vr[3][nn >> 1], vr[2][nn >> 1], sel);
-        const s16x4 av = __builtin_bit_cast(s16x4, (uint2){d0, d1});
-        a.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, a.o[nn], 0, 0, 0);
-    }
+    for (int nn = 0; nn < 8; nn++)
+        a.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_op(nn), pb, a.o[nn], 0, 0, 0);
+}
+
+// The tile step on V as loaded by load_tile_rows: product nn takes dim
+// 8*row16 + nn of the lane group's 4 tokens, transposed in registers.
+template <bool kMaybeEmpty>
+__device__ __forceinline__ void tile_update(const u32x4 (&kr)[4], const u32x4 (&vr)[4],
+                                            const bf16x8 (&qv)[4], int nv, float scale_log2,
+                                            Acc &a, Lane ln) {
+    tile_update_v<kMaybeEmpty>(
+        kr,
+        [&](int nn) {
+            // word nn/2 of each row, low half for even nn, high half for odd nn
+            const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t d0 = __builtin_amdgcn_perm(vr[1][nn >> 1], vr[0][nn >> 1], sel);
+            const uint32_t d1 = __builtin_amdgcn_perm(vr[3][nn >> 1], vr[2][nn >> 1], sel);
+            return __builtin_bit_cast(s16x4, (uint2){d0, d1});
+        },
+        qv, nv, scale_log2, a, ln);
 }
 
 // Issue the 8 sixteen-byte loads of one (block, KV head) tile through buffer

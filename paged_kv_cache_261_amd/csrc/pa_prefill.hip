@@ -193,15 +193,35 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
             *(u32x4 *)(base + lo + (c & 15) * 16) = gr[j];
         }
     };
-    // the tile step's operands out of a stage (the layout load_tile_rows gives)
-    auto stage_read = [&](int st, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+    // The tile step's operands out of a stage.  K: the layout load_tile_rows
+    // gives.  V: P.V product nn covers dims 16 nn .. 16 nn + 15 (not
+    // 8 m + nn as in the decode kernels); lane L = row16 of group grp reads
+    // the 8 bytes of row 4 grp + L / 4 at dims 16 nn + 4 (L % 4), and the
+    // transposing LDS read (within each 16 lanes, lane i takes element i % 4
+    // of the reads of lanes i / 4 + 4 k, k = 0..3) hands lane (m, grp) dim
+    // 16 nn + m of tokens 4 grp .. 4 grp + 3: the operand the product takes,
+    // with no byte permutes.
+    auto stage_read = [&](int st, u32x4 (&kr)[4], s16x4 (&vt)[8]) {
         const char *base = lds + st * kStage;
 #pragma unroll
         for (int j = 0; j < 4; j++)
             kr[j] = *(const u32x4 *)(base + ln.row16 * kLdsRowK + ln.grp * 16 + 64 * j);
+        const char *vrow =
+            base + kVBase + (4 * ln.grp + (ln.row16 >> 2)) * kLdsRowV + (ln.row16 & 3) * 8;
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            vr[j] = *(const u32x4 *)(base + kVBase + (4 * ln.grp + j) * kLdsRowV + ln.row16 * 16);
+        for (int nn = 0; nn < 8; nn++)
+            vt[nn] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(vrow + 32 * nn));
+    };
+    // O / l of column row16 in bfloat16: a.o[nn][i] holds dim 16 nn + 4 grp + i
+    auto store_out_row = [&](char *out_row, const Acc &acc) {
+        const float inv = acc.lsum > 0.f ? 1.f / acc.lsum : 0.f;
+        char *dst = out_row + 8 * ln.grp;
+#pragma unroll
+        for (int nn = 0; nn < 8; nn++)
+            *(uint2 *)(dst + 32 * nn) =
+                (uint2){pack_bf16x2(acc.o[nn][0] * inv, acc.o[nn][1] * inv),
+                        pack_bf16x2(acc.o[nn][2] * inv, acc.o[nn][3] * inv)};
     };
 
     // tile x is loaded into register set x % 2 three iterations ahead and
@@ -218,13 +238,14 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
         for (int j = 0; j < 2; j++) {
             const int t = t0 + j;
             if (t >= ntiles) break;
-            u32x4 kr[4], vr[4];
-            stage_read(j, kr, vr);
+            u32x4 kr[4];
+            s16x4 vt[8];
+            stage_read(j, kr, vt);
             if ((unsigned)ph0 < (unsigned)p.num_blocks) {
 #pragma unroll
                 for (int cg = 0; cg < kPrefillGroups; cg++)
-                    tile_update<true>(kr, vr, qv[cg], ncol[cg] - t * kTile, p.scale_log2,
-                                      a[cg], ln);
+                    tile_update_v<true>(kr, [&](int nn) { return vt[nn]; }, qv[cg],
+                                        ncol[cg] - t * kTile, p.scale_log2, a[cg], ln);
             }
             if (t + 1 < ntiles) stage_write(j ^ 1, gr[j ^ 1]);
             issue(t + 3, ph3, gr[j ^ 1]);
@@ -239,8 +260,8 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
     for (int cg = 0; cg < kPrefillGroups; cg++) {
         acc_finish(a[cg]);
         if (ok[cg])
-            store_row((char *)out + ((size_t)rowid[cg] * p.num_q_heads + head[cg]) * kD * 2,
-                      a[cg], ln);
+            store_out_row((char *)out + ((size_t)rowid[cg] * p.num_q_heads + head[cg]) * kD * 2,
+                          a[cg]);
     }
 }
 
