@@ -906,6 +906,20 @@ def test_prefill_matches_oracle(G, bs):
     H.assert_close_to_oracle(got, ref, "bf16", f"prefill G {G} bs {bs}")
 
 
+def test_prefill_more_sequences_than_lanes():
+    """70 sequences: past 64 the kernel dispatches groups in plain order
+    instead of ranking the context lengths one lane per sequence; chunks of
+    0 to 40 rows over prefixes of 0 to 300 keys, workgroups whose last
+    wavefronts have no rows."""
+    rng = np.random.default_rng(70)
+    chunks = [int(x) for x in rng.integers(0, 41, size=70)]
+    prefixes = [int(x) for x in rng.integers(0, 301, size=70)]
+    q, cu, ctx, kc, vc, tab = prefill_gpu_case(rng, chunks, prefixes, 8, 2, 16)
+    ref = pao.prefill_concat(q, kc, vc, tab, cu, ctx, 0.09)
+    got = gpu_prefill(q, H.to_dev(kc), H.to_dev(vc), tab, cu, ctx, 0.09)
+    H.assert_close_to_oracle(got, ref, "bf16", "prefill, 70 sequences")
+
+
 def test_prefill_of_one_row_equals_decode():
     """A chunk of one row is the decode of that query (same tile step)."""
     rng = np.random.default_rng(3)
