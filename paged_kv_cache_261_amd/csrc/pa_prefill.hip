@@ -12,12 +12,13 @@
 // How (matrix cores; bf16, head_dim 128, block_size >= 16, group size
 // G <= 16): one wavefront serves 16 query-head columns of one KV head (16 x
 // kPrefillGroups with the compile-time knob) -- the G heads of TPU = 16 / G
-// consecutive chunk rows -- and walks the keys 0 .. (the last row's position)
-// in 16-token tiles with the tile step of pa_mfma_tile.h; a column's causal
-// limit is its row's position, so the last tiles are partly masked per
-// column.  A workgroup of kWgWaves such wavefronts (consecutive units of one
-// (sequence, KV head)) reads each K/V tile from memory once and shares it
-// through LDS.
+// consecutive chunk rows -- and walks the keys 0 .. (the last row's
+// position) two 16-token tiles at a time: both score products (the decode
+// tile step's layouts), one online-softmax update over the 32 keys, and P.V
+// on the 16x16x32 matrix-core product; a column's causal limit is its row's
+// position, so the last tiles are partly masked per column.  A workgroup of
+// kWgWaves such wavefronts (consecutive units of one (sequence, KV head))
+// reads each K/V tile from memory once and shares it through LDS.
 //
 // Order of the workgroups: a unit's work grows with its sequence's context
 // and its rows' positions, and the grid is many times larger than what is
@@ -58,15 +59,14 @@ constexpr int kPrefillCols = kPrefillColumns;
 // ---------------------------------------------------------------------------
 // Each tile (16 rows of K and of V, 8 KiB) is read from memory once per
 // workgroup in 16-byte pieces, so every request covers whole 128-byte
-// lines; the wavefronts then read the tile out of LDS in exactly the
-// register layout of the tile step, so the arithmetic -- and every output
-// bit -- is that of a wavefront loading the tile itself.  LDS rows are
-// padded (below), so the 16 lanes that read one column of 16 K rows do not
-// all fall in the same banks.  Two stages alternate: while tile t is read
-// and computed out of one, tile t+1 is written into the other and tile t+3
-// is loaded (two register sets hold the tiles in flight, so a load has two
-// iterations to arrive); one LDS-only barrier per tile (no wait on the
-// loads in flight).
+// lines; the wavefronts then read their operands out of LDS: K in the
+// register layout of the decode tile step, V through the transposing LDS
+// read.  LDS rows are padded (below), so the 16 lanes that read one column
+// of 16 K rows do not all fall in the same banks.  Four stages form a ring:
+// while tiles 2p and 2p+1 are read and computed out of two of them, tiles
+// 2p+2 and 2p+3 (loaded during the step before) are written into the other
+// two and tiles 2p+4 and 2p+5 are loaded; one LDS-only barrier per step (no
+// wait on the loads in flight).
 // ---------------------------------------------------------------------------
 #ifndef PA_PREFILL_WG_WAVES
 #define PA_PREFILL_WG_WAVES 4
@@ -97,12 +97,95 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Two consecutive tiles A and B in one step: both score products, one
+// softmax update over their 32 keys, and P.V as one
+// v_mfma_f32_16x16x32_bf16 per product whose k slots 8 grp .. 8 grp + 3
+// hold tile A's tokens 4 grp .. 4 grp + 3 and 8 grp + 4 .. 8 grp + 7 tile
+// B's -- the order in which the lane holds P.  okA / okB: the tile's block
+// id is valid (a tile with an invalid id contributes nothing).
+// The operands come straight out of the two stages, K of A, then K of B,
+// then V, with scheduling fences between, so no more than one tile's K or
+// both tiles' V are in registers at a time (the step fits four wavefronts
+// per SIMD).
+__device__ __forceinline__ void read_k(const char *stage, Lane ln, u32x4 (&kr)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        kr[j] = *(const u32x4 *)(stage + ln.row16 * kLdsRowK + ln.grp * 16 + 64 * j);
+}
+__device__ __forceinline__ s16x4 read_vt(const char *stage, Lane ln, int nn) {
+    const char *vrow =
+        stage + kVBase + (4 * ln.grp + (ln.row16 >> 2)) * kLdsRowV + (ln.row16 & 3) * 8;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(vrow + 32 * nn));
+}
+__device__ __forceinline__ void pair_update(const char *stA, const char *stB,
+                                            const bf16x8 (&qv)[4], int nv, bool okA, bool okB,
+                                            float scale_log2, Acc &a, Lane ln) {
+    f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = {0.f, 0.f, 0.f, 0.f};
+    {
+        u32x4 kr[4];
+        read_k(stA, ln, kr);
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++)
+            SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
+                                                         qv[kk], SA, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        u32x4 kr[4];
+        read_k(stB, ln, kr);
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++)
+            SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
+                                                         qv[kk], SB, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        s[i] = okA && 4 * ln.grp + i < nv ? SA[i] * scale_log2 : -INFINITY;
+        s[4 + i] = okB && 4 * ln.grp + i + kTile < nv ? SB[i] * scale_log2 : -INFINITY;
+    }
+    const float lmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                             fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    const float tmax = xor32_max(xor16_max(lmax));
+#if PA_RESCALE_SLACK > 0
+    const float m_new = tmax > a.m + (float)PA_RESCALE_SLACK ? tmax : a.m;
+#else
+    const float m_new = fmaxf(a.m, tmax);
+#endif
+    const float shift = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(a.m - shift);
+    float pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) pr[i] = fast_exp2(s[i] - shift);
+    a.lsum = a.lsum * alpha +
+             (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+    a.m = m_new;
+    if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int nn = 0; nn < 8; nn++) a.o[nn] *= alpha;
+    }
+    const bf16x8 pb = __builtin_bit_cast(
+        bf16x8, (u32x4){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nn = 0; nn < 8; nn++) {
+        const uint2 x = __builtin_bit_cast(uint2, read_vt(stA, ln, nn));
+        const uint2 y = __builtin_bit_cast(uint2, read_vt(stB, ln, nn));
+        a.o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, (u32x4){x.x, x.y, y.x, y.y}), pb, a.o[nn], 0, 0, 0);
+    }
+}
+constexpr int kStages = 4;
+
 __global__ __launch_bounds__(kWgThreads)
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
 void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ tables,
                          const int32_t *__restrict__ cu_q, const int32_t *__restrict__ ctx_lens,
                          void *__restrict__ out) {
-    __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
+    __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
     const PrefillParams &p = args;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -193,26 +276,6 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
             *(u32x4 *)(base + lo + (c & 15) * 16) = gr[j];
         }
     };
-    // The tile step's operands out of a stage.  K: the layout load_tile_rows
-    // gives.  V: P.V product nn covers dims 16 nn .. 16 nn + 15 (not
-    // 8 m + nn as in the decode kernels); lane L = row16 of group grp reads
-    // the 8 bytes of row 4 grp + L / 4 at dims 16 nn + 4 (L % 4), and the
-    // transposing LDS read (within each 16 lanes, lane i takes element i % 4
-    // of the reads of lanes i / 4 + 4 k, k = 0..3) hands lane (m, grp) dim
-    // 16 nn + m of tokens 4 grp .. 4 grp + 3: the operand the product takes,
-    // with no byte permutes.
-    auto stage_read = [&](int st, u32x4 (&kr)[4], s16x4 (&vt)[8]) {
-        const char *base = lds + st * kStage;
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            kr[j] = *(const u32x4 *)(base + ln.row16 * kLdsRowK + ln.grp * 16 + 64 * j);
-        const char *vrow =
-            base + kVBase + (4 * ln.grp + (ln.row16 >> 2)) * kLdsRowV + (ln.row16 & 3) * 8;
-#pragma unroll
-        for (int nn = 0; nn < 8; nn++)
-            vt[nn] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(vrow + 32 * nn));
-    };
     // O / l of column row16 in bfloat16: a.o[nn][i] holds dim 16 nn + 4 grp + i
     auto store_out_row = [&](char *out_row, const Acc &acc) {
         const float inv = acc.lsum > 0.f ? 1.f / acc.lsum : 0.f;
@@ -224,37 +287,41 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
                         pack_bf16x2(acc.o[nn][2] * inv, acc.o[nn][3] * inv)};
     };
 
-    // tile x is loaded into register set x % 2 three iterations ahead and
-    // written to its stage at the end of the iteration before its own
+    // tiles 2p and 2p+1 are computed in step p out of stages (2p) % 4 and
+    // (2p+1) % 4; tiles 2p+2, 2p+3 (loaded during step p-1) are written into
+    // the stages step p-1 read, and tiles 2p+4, 2p+5 are loaded.  Tiles past
+    // the last are written too (as zeros: their loads read nothing), so no
+    // stale LDS bits meet a zero probability.
+    const int ntiles2 = (ntiles + 1) & ~1;
     u32x4 gr[2][kPiecesPerThread];
-    int ph0 = phys_of(0), ph1 = phys_of(1), ph2 = phys_of(2), ph3 = phys_of(3);
-    issue(0, ph0, gr[0]);
+    int phA = phys_of(0), phB = phys_of(1);
+    issue(0, phA, gr[0]);
+    issue(1, phB, gr[1]);
     stage_write(0, gr[0]);
-    issue(1, ph1, gr[1]);
-    issue(2, ph2, gr[0]);
+    stage_write(1, gr[1]);
+    int phC = phys_of(2), phD = phys_of(3);
+    issue(2, phC, gr[0]);
+    issue(3, phD, gr[1]);
     lds_barrier();
-    for (int t0 = 0; t0 < ntiles; t0 += 2) {
+    for (int t = 0; t < ntiles; t += 2) {
+        const int sa = t & 3;
+        const bool okA = (unsigned)phA < (unsigned)p.num_blocks;
+        const bool okB = (unsigned)phB < (unsigned)p.num_blocks;
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int t = t0 + j;
-            if (t >= ntiles) break;
-            u32x4 kr[4];
-            s16x4 vt[8];
-            stage_read(j, kr, vt);
-            if ((unsigned)ph0 < (unsigned)p.num_blocks) {
-#pragma unroll
-                for (int cg = 0; cg < kPrefillGroups; cg++)
-                    tile_update_v<true>(kr, [&](int nn) { return vt[nn]; }, qv[cg],
-                                        ncol[cg] - t * kTile, p.scale_log2, a[cg], ln);
-            }
-            if (t + 1 < ntiles) stage_write(j ^ 1, gr[j ^ 1]);
-            issue(t + 3, ph3, gr[j ^ 1]);
-            ph0 = ph1;
-            ph1 = ph2;
-            ph2 = ph3;
-            ph3 = phys_of(t + 4);
-            lds_barrier();
+        for (int cg = 0; cg < kPrefillGroups; cg++)
+            pair_update(lds + sa * kStage, lds + (sa + 1) * kStage, qv[cg], ncol[cg] - t * kTile,
+                        okA, okB, p.scale_log2, a[cg], ln);
+        if (t + 2 < ntiles2) {
+            stage_write((t + 2) & 3, gr[0]);
+            stage_write((t + 3) & 3, gr[1]);
         }
+        issue(t + 4, phys_of(t + 4), gr[0]);
+        issue(t + 5, phys_of(t + 5), gr[1]);
+        phA = phC;
+        phB = phD;
+        phC = phys_of(t + 4);
+        phD = phys_of(t + 5);
+        lds_barrier();
     }
 #pragma unroll
     for (int cg = 0; cg < kPrefillGroups; cg++) {

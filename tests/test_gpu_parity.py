@@ -921,7 +921,10 @@ def test_prefill_more_sequences_than_lanes():
 
 
 def test_prefill_of_one_row_equals_decode():
-    """A chunk of one row is the decode of that query (same tile step)."""
+    """A chunk of one row is the decode of that query: both match the
+    oracle, and each other within the bf16 tolerance (prefill takes one
+    softmax step per 32 keys and sums P.V in 32-key products, decode per
+    16 keys, so their roundings differ)."""
     rng = np.random.default_rng(3)
     chunks, prefixes = [1, 1, 1, 1], [0, 15, 300, 1024]
     q, cu, ctx, kc, vc, tab = prefill_gpu_case(rng, chunks, prefixes, 32, 8, 16)
@@ -930,7 +933,8 @@ def test_prefill_of_one_row_equals_decode():
     b = H.gpu_decode(q, kd, vd, tab, ctx, 0.1, None, 0, MFMA)
     ref = pao.decode_concat(q, kc, vc, tab, ctx, 0.1)
     H.assert_close_to_oracle(a, ref, "bf16", "prefill of one row")
-    np.testing.assert_array_equal(a, b)
+    H.assert_close_to_oracle(b, ref, "bf16", "decode")
+    assert H.row_rel_err(a, b).max() <= 1e-2
 
 
 def test_prefill_whole_prompt_then_decode():
