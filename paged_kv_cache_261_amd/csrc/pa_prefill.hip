@@ -104,9 +104,9 @@ __device__ __forceinline__ void lds_barrier() {
 // B's -- the order in which the lane holds P.  okA / okB: the tile's block
 // id is valid (a tile with an invalid id contributes nothing).
 // The operands come straight out of the two stages, K of A, then K of B,
-// then V, with scheduling fences between, so no more than one tile's K or
-// both tiles' V are in registers at a time (the step fits four wavefronts
-// per SIMD).
+// then V, with scheduling fences between the score products, so no more
+// than one tile's K is in registers at a time (the step fits four
+// wavefronts per SIMD).
 __device__ __forceinline__ void read_k(const char *stage, Lane ln, u32x4 (&kr)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; j++)
@@ -118,6 +118,11 @@ __device__ __forceinline__ s16x4 read_vt(const char *stage, Lane ln, int nn) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4 *)(vrow + 32 * nn));
 }
+// scheduling fences in the pair step: bit 0 after tile A's scores, bit 1
+// after tile B's, bit 2 before the V reads (measured: 3 best, 0.2% over 7)
+#ifndef PA_PAIR_FENCES
+#define PA_PAIR_FENCES 3
+#endif
 __device__ __forceinline__ void pair_update(const char *stA, const char *stB,
                                             const bf16x8 (&qv)[4], int nv, bool okA, bool okB,
                                             float scale_log2, Acc &a, Lane ln) {
@@ -130,7 +135,7 @@ __device__ __forceinline__ void pair_update(const char *stA, const char *stB,
             SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
                                                          qv[kk], SA, 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if (PA_PAIR_FENCES & 1) __builtin_amdgcn_sched_barrier(0);
     {
         u32x4 kr[4];
         read_k(stB, ln, kr);
@@ -139,7 +144,7 @@ __device__ __forceinline__ void pair_update(const char *stA, const char *stB,
             SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
                                                          qv[kk], SB, 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if (PA_PAIR_FENCES & 2) __builtin_amdgcn_sched_barrier(0);
     float s[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -169,7 +174,7 @@ __device__ __forceinline__ void pair_update(const char *stA, const char *stB,
     const bf16x8 pb = __builtin_bit_cast(
         bf16x8, (u32x4){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                         pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
-    __builtin_amdgcn_sched_barrier(0);
+    if (PA_PAIR_FENCES & 4) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int nn = 0; nn < 8; nn++) {
         const uint2 x = __builtin_bit_cast(uint2, read_vt(stA, ln, nn));
