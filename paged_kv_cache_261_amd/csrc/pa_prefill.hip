@@ -69,7 +69,7 @@ constexpr int kPrefillCols = kPrefillColumns;
 // wait on the loads in flight).
 // ---------------------------------------------------------------------------
 #ifndef PA_PREFILL_WG_WAVES
-#define PA_PREFILL_WG_WAVES 4
+#define PA_PREFILL_WG_WAVES 8
 #endif
 constexpr int kWgWaves = PA_PREFILL_WG_WAVES;
 constexpr int kWgThreads = kWave * kWgWaves;
