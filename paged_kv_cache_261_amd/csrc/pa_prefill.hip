@@ -145,11 +145,14 @@ __device__ __forceinline__ void pair_update(const char *stA, const char *stB,
                                                          qv[kk], SB, 0, 0, 0);
     }
     if (PA_PAIR_FENCES & 2) __builtin_amdgcn_sched_barrier(0);
+    // visible rows of each tile for this column (none when its block id is invalid)
+    const int limA = okA ? nv : 0;
+    const int limB = okB ? nv - kTile : 0;
     float s[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        s[i] = okA && 4 * ln.grp + i < nv ? SA[i] * scale_log2 : -INFINITY;
-        s[4 + i] = okB && 4 * ln.grp + i + kTile < nv ? SB[i] * scale_log2 : -INFINITY;
+        s[i] = 4 * ln.grp + i < limA ? SA[i] * scale_log2 : -INFINITY;
+        s[4 + i] = 4 * ln.grp + i < limB ? SB[i] * scale_log2 : -INFINITY;
     }
     const float lmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
                              fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
@@ -257,18 +260,17 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
         const int rows = in ? min(kTile, kmax - t * kTile) : 0;
         const size_t off = ((((size_t)(in ? phys : 0) * p.num_kv_heads + g) << log2bs) +
                             ((t * kTile) & bs_mask)) * (size_t)kRowBytes;
-        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(kbase + off), (short)0, rows * kRowBytes, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(vbase + off), (short)0, rows * kRowBytes, kRsrcWord3);
 #pragma unroll
         for (int j = 0; j < kPiecesPerThread; j++) {
             const int c = tid + j * kWgThreads;
             const int goff = ((c >> 4) & (kTile - 1)) * kRowBytes + (c & 15) * 16;
-            // K or V is the same for the whole wavefront (256 is a multiple of 64)
+            // K or V is the same for the whole wavefront (256 is a multiple of
+            // 64), so only that pool's descriptor is built
             const bool of_k = wave * kWave + j * kWgThreads < kPieces / 2;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((of_k ? kbase : vbase) + off), (short)0, rows * kRowBytes, kRsrcWord3);
             gr[j] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(of_k ? krs : vrs, goff, 0, kReuseAux));
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, goff, 0, kReuseAux));
         }
     };
     auto stage_write = [&](int st, const u32x4 (&gr)[kPiecesPerThread]) {
