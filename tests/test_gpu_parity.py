@@ -522,6 +522,57 @@ def test_pool_beyond_4gib(dtype):
     torch.cuda.empty_cache()
 
 
+def _drop_block(tab, ctx, j, bs):
+    """Tables and lengths of the same sequences with their full logical block
+    j removed (later blocks move up one entry)."""
+    out = np.full_like(tab, -1)
+    for b in range(tab.shape[0]):
+        row = [int(x) for i, x in enumerate(tab[b]) if i != j]
+        out[b, :len(row)] = row
+    return out, np.asarray(ctx) - bs
+
+
+@pytest.mark.parametrize("part,algo", [(0, MFMA), (512, MFMA), (-2, MFMA), (-3, MFMA),
+                                       (0, VECTOR), (512, VECTOR), (-2, VECTOR)])
+def test_out_of_range_block_is_left_out(part, algo):
+    """A block-table entry outside [0, num_blocks) is never read and the tokens
+    it would hold are left out: decode with logical block 2 of every sequence
+    pointing past the pool equals the oracle over the same sequences with that
+    block removed."""
+    rng = np.random.default_rng(123)
+    hkv, G, d, bs = 2, 4, 128, 16
+    ctxs = [100, 300, 48, 1000]
+    q = S._normal(rng, (len(ctxs), hkv * G, d), "bf16")
+    kl = [S._normal(rng, (n, hkv, d), "bf16") for n in ctxs]
+    vl = [S._normal(rng, (n, hkv, d), "bf16") for n in ctxs]
+    nb = sum((n + bs - 1) // bs for n in ctxs) + 4
+    kc, vc, tab = H.paginate(kl, vl, bs, nb, rng, "bf16")
+    ctx = np.array(ctxs, dtype=np.int32)
+    bad = tab.copy()
+    bad[:, 2] = [nb, nb + 7, 1 << 30, -5]
+    tab_ref, ctx_ref = _drop_block(tab, ctx, 2, bs)
+    ref = pao.decode_concat(q, kc, vc, tab_ref, ctx_ref, 1 / math.sqrt(d))
+    got = H.gpu_decode(q, H.to_dev(kc), H.to_dev(vc), bad, ctx, 1 / math.sqrt(d), None, part,
+                       algo)
+    H.assert_close_to_oracle(got, ref, "bf16", f"mode {part} algo {algo}")
+
+
+def test_prefill_out_of_range_block_is_left_out():
+    """The same for prefill: logical block 1 (inside every cached prefix)
+    points past the pool; the chunk rows equal the oracle's over the
+    sequences with that block removed."""
+    rng = np.random.default_rng(124)
+    chunks, prefixes = [40, 17, 1, 64], [100, 64, 32, 500]
+    q, cu, ctx, kc, vc, tab = prefill_gpu_case(rng, chunks, prefixes, 8, 2, 16)
+    nb = kc.shape[0]
+    bad = tab.copy()
+    bad[:, 1] = [nb, nb + 3, 1 << 29, -1]
+    tab_ref, ctx_ref = _drop_block(tab, ctx, 1, 16)
+    ref = pao.prefill_concat(q, kc, vc, tab_ref, cu, ctx_ref, 0.09)
+    got = gpu_prefill(q, H.to_dev(kc), H.to_dev(vc), bad, cu, ctx, 0.09)
+    H.assert_close_to_oracle(got, ref, "bf16", "prefill with an out-of-range block")
+
+
 @pytest.mark.parametrize("part", [512, -2, -3])
 def test_phases_equal_one_call(part):
     w, kd, vd, kh, vh = full("long_split_bf16")
