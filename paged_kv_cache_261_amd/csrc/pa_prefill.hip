@@ -322,12 +322,12 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
             stage_write((t + 2) & 3, gr[0]);
             stage_write((t + 3) & 3, gr[1]);
         }
-        issue(t + 4, phys_of(t + 4), gr[0]);
-        issue(t + 5, phys_of(t + 5), gr[1]);
         phA = phC;
         phB = phD;
         phC = phys_of(t + 4);
         phD = phys_of(t + 5);
+        issue(t + 4, phC, gr[0]);
+        issue(t + 5, phD, gr[1]);
         lds_barrier();
     }
 #pragma unroll
