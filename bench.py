@@ -288,7 +288,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"metric": METRIC, "error": "this build measures one GPU only: the "
+        print(json.dumps({"metric": METRIC, "error": "the benchmark measures one GPU: the "
                           "decode path has no multi-GPU mode; run with --gpus 1"}))
         sys.exit(2)
 

@@ -1,7 +1,7 @@
 """Compile the CPU oracle (``oracle/pao.c``) into ``oracle/liboracle.so``.
 
-Test infrastructure only: this builds the checker, nothing in the product
-library uses it.  Plain ``gcc -std=c11 -O2`` (no fast-math, so float64 sums
+Test infrastructure only: it compiles the reference the tests compare
+against; nothing in the product library uses it.  Plain ``gcc -std=c11 -O2`` (no fast-math, so float64 sums
 keep their written order) with OpenMP for the outer (sequence, head) loops.
 """
 import os
