@@ -156,9 +156,15 @@ __global__ __launch_bounds__(D) void reduce_kernel(const ReduceParams p) {
     const int b = row / p.num_q_heads;
     const int n = clamp_ctx(p.context_lens[b], p.max_context_len);
     const int n_parts = (n + p.partition_size - 1) / p.partition_size;
-    if (n_parts <= 1) return;                   // phase 1 wrote the output itself
-    const size_t prow = (size_t)row * p.num_partitions;
     T *out = (T *)p.out + (size_t)row * D;
+    if (n_parts == 0) {
+        // an empty context has no tiles, so the matrix-core split never
+        // visits it: its row is zeros, written here
+        store_out(out + threadIdx.x, 0.f);
+        return;
+    }
+    if (n_parts == 1) return;                   // phase 1 wrote the output itself
+    const size_t prow = (size_t)row * p.num_partitions;
     if (merge_row_sparse<T, D>(out, n_parts, p.ws_m + prow, p.ws_l + prow, p.ws_acc + prow * D, D))
         return;
     merge_row<T, D>(out, n_parts, p.ws_m + prow, p.ws_l + prow, 1, p.ws_acc + prow * D, D,

@@ -143,7 +143,9 @@ def gpu_decode(q, k_cache, v_cache, tables, ctx, scale, max_context_len=None,
     td = to_dev(np.asarray(tables, dtype=np.int32))
     cd = to_dev(np.asarray(ctx, dtype=np.int32))
     mc = int(np.max(ctx)) if max_context_len is None else int(max_context_len)
-    out = torch.empty_like(qd)
+    # NaN-filled, so a row no kernel writes shows up as non-finite (a fresh
+    # torch.empty_like would often hand back the previous call's output)
+    out = torch.full_like(qd, float("nan"))
     ws = pa.workspace_for(qd, k_cache, mc, partition)
     pa.pa_decode(out, qd, k_cache, v_cache, td, cd, scale, mc, partition, ws, algo)
     torch.cuda.synchronize()

@@ -196,3 +196,29 @@ def test_beam_sharing_saves_blocks_and_copies_only_shared_tails():
             if pos[i] % bs == 0:
                 assert slot // bs not in copied
     assert w.n_copies > 0
+
+
+# --------------------------------------------------------------------------
+# chunked-prefill workload
+# --------------------------------------------------------------------------
+def test_prefill_layout_matches_oracle_pool():
+    """The chunked-prefill workload's tables and slot mappings equal the
+    oracle pool's when each sequence appends its prefix and then its chunk,
+    sequence by sequence, from the same free stack."""
+    from oracle import Pool
+    w = S.make_prefill_workload("prefill_bf16")
+    c = w.cfg
+    free_order = np.random.default_rng([c.seed, 3]).permutation(c.num_blocks).astype(np.int32)
+    pool = Pool(c.num_blocks, c.block_size, free_order=free_order)
+    prefix_slots, chunk_slots, tables = [], [], []
+    for b in range(c.num_seqs):
+        s = pool.seq_new()
+        prefix_slots.extend(pool.append(s)[0] for _ in range(int(w.prefix_lens[b])))
+        chunk_slots.extend(pool.append(s)[0] for _ in range(int(w.chunk_lens[b])))
+        tables.append(pool.table(s, c.max_blocks_per_seq))
+        assert pool.seq_len(s) == w.ctx[b]
+    np.testing.assert_array_equal(np.stack(tables), w.tables)
+    np.testing.assert_array_equal(np.array(prefix_slots), w.prefix_slots)
+    np.testing.assert_array_equal(np.array(chunk_slots), w.chunk_slots)
+    np.testing.assert_array_equal(np.diff(w.cu_seqlens_q), w.chunk_lens)
+    assert pool.stats()["n_copies"] == 0
