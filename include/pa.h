@@ -72,7 +72,9 @@ enum {
     PA_ERR_WORKSPACE = -4,    /* workspace missing or smaller than required      */
     PA_ERR_LAUNCH = -5,       /* the HIP runtime refused a kernel launch         */
     PA_ERR_ALGO = -6,         /* requested kernel variant cannot run this shape  */
-    PA_ERR_ALIGN = -7         /* a tensor pointer is not 16-byte aligned          */
+    PA_ERR_ALIGN = -7,        /* a tensor pointer is not 16-byte aligned          */
+    PA_ERR_SCRATCH = -8       /* pa_decode_noalloc: the problem's workspace is
+                                 larger than the static scratch                  */
 };
 
 /* Special partition_size values for pa_decode / pa_decode_partitions /
@@ -292,6 +294,36 @@ int pa_decode_partitions(void *out, const void *q, const void *k_cache, const vo
 int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int num_q_heads,
                      int num_kv_heads, int head_dim, int max_context_len, int partition_size,
                      const void *workspace, size_t workspace_bytes, int dtype, void *stream);
+
+/*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Arguments and results are those of pa_decode without
+ * the workspace.  Split modes use scratch the library holds instead: a
+ * file-scope device array of PA_NOALLOC_SCRATCH_BYTES on every GPU the
+ * library runs on, kept until the process ends.  Its device address is
+ * looked up on the first call on each device (the device of `stream`, or
+ * the current device for the default stream); no call allocates or frees
+ * device memory.
+ *
+ * A problem whose workspace (pa_decode_workspace_size for the partition
+ * mode the call resolves to) is larger than the scratch returns
+ * PA_ERR_SCRATCH with nothing enqueued; a failed address lookup returns
+ * PA_ERR_LAUNCH.  Single-pass decode (partition_size 0, or the library's
+ * choice of it) uses no scratch.
+ *
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (nothing in it needs clearing: each call writes every
+ * piece before reading it).  Calls that may overlap on one GPU -- on
+ * different streams, or from host threads without ordering -- race on it
+ * and give wrong results: order them on one stream.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int num_blocks,
+                      int block_size, int max_blocks_per_seq, int max_context_len, float scale,
+                      int partition_size, int dtype, int algo, void *stream);
 
 /* A static, human-readable name for a status code. */
 const char *pa_status_string(int status);

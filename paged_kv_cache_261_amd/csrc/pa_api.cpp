@@ -3,10 +3,19 @@
 // Nothing here allocates device memory or synchronises.
 #include "pa.h"
 
+#include <atomic>
 #include <initializer_list>
 #include <math.h>
+#include <mutex>
 
 #include "pa_internal.h"
+
+// Scratch of pa_decode_noalloc: one file-scope device array, so every GPU
+// the library runs on holds its own copy (PA_NOALLOC_SCRATCH_BYTES) until
+// the process ends.  In host code `scratch` is only a stand-in for the
+// symbol: its device address on each GPU comes from hipGetSymbolAddress
+// (scratch_on below) and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -200,6 +209,19 @@ int balanced_kernel(const DecodeArgs &a) {
     return -1;
 }
 
+// The kernels of a resolved split mode can run these arguments: PA_OK, or
+// why not.
+int check_split_mode(const DecodeArgs &a, int partition) {
+    if (partition == PA_PARTITION_SHARED) {
+        if (!mfma_applies(a) || a.algo == PA_ALGO_VECTOR) return PA_ERR_ALGO;
+    } else if (partition == PA_PARTITION_BALANCED) {
+        if (balanced_kernel(a) < 0) return PA_ERR_ALGO;
+    } else if (partition <= 0 || partition % a.block_size) {
+        return PA_ERR_SHAPE;
+    }
+    return PA_OK;
+}
+
 // Phase 1 (or the whole decode when num_partitions == 1).
 int launch_units(const DecodeArgs &a, int partition, int num_partitions, float *ws_m,
                  float *ws_l, float *ws_acc, hipStream_t stream) {
@@ -284,6 +306,36 @@ pa::SharedParams shared_params(const DecodeArgs &a, const WorkspaceLayout &w, ch
     return p;
 }
 
+// Device address of `scratch` on each device, looked up once per device
+// with that device current.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+hipError_t scratch_on(int device, void **ptr) {
+    void *p = g_scratch[device].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch[device].load(std::memory_order_relaxed);
+        if (!p) {
+            int current = -1;
+            hipError_t e = hipGetDevice(&current);
+            if (e != hipSuccess) return e;
+            if (current != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (current != device) {
+                const hipError_t back = hipSetDevice(current);
+                if (e == hipSuccess) e = back;
+            }
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch[device].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,6 +350,8 @@ const char *pa_status_string(int status) {
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_ALGO: return "requested kernel variant does not support this shape";
     case PA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case PA_ERR_SCRATCH:
+        return "the problem needs more workspace than the library's static scratch holds";
     default: return "unknown status";
     }
 }
@@ -445,13 +499,8 @@ int pa_decode_partitions(void *out, const void *q, const void *k_cache, const vo
     if (rc != PA_OK) return rc;
     const int partition = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads,
                                             head_dim, block_size, max_context_len, dtype, algo);
-    if (partition == PA_PARTITION_SHARED) {
-        if (!mfma_applies(a) || algo == PA_ALGO_VECTOR) return PA_ERR_ALGO;
-    } else if (partition == PA_PARTITION_BALANCED) {
-        if (balanced_kernel(a) < 0) return PA_ERR_ALGO;
-    } else if (partition <= 0 || partition % block_size) {
-        return PA_ERR_SHAPE;
-    }
+    rc = check_split_mode(a, partition);
+    if (rc != PA_OK) return rc;
     if (num_seqs == 0) return PA_OK;
     const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, max_context_len, partition,
                                      num_q_heads / num_kv_heads);
@@ -548,6 +597,46 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
     if (rc != PA_OK) return rc;
     return pa_decode_reduce(out, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                             max_context_len, partition, workspace, workspace_bytes, dtype, stream);
+}
+
+int pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int num_blocks,
+                      int block_size, int max_blocks_per_seq, int max_context_len, float scale,
+                      int partition_size, int dtype, int algo, void *stream) {
+    const DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                       max_blocks_per_seq, max_context_len, scale, dtype, algo};
+    const int rc = validate_decode(a);
+    if (rc != PA_OK) return rc;
+    const int partition = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads,
+                                            head_dim, block_size, max_context_len, dtype, algo);
+    if (!is_split_mode(partition) && (partition < 0 || (partition > 0 && partition % block_size)))
+        return PA_ERR_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (partition == 0)   // single pass: no workspace at all
+        return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                         num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                         max_blocks_per_seq, max_context_len, scale, 0, nullptr, 0, dtype, algo,
+                         stream);
+    const int mode = check_split_mode(a, partition);
+    if (mode != PA_OK) return mode;
+    const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, max_context_len, partition,
+                                     num_q_heads / num_kv_heads);
+    if (w.total > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+    if (w.num_partitions > pa::kMaxPartitions) return PA_ERR_SHAPE;
+    int device = -1;
+    const hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &device)
+                                : hipGetDevice(&device);
+    if (e != hipSuccess || device < 0 || device >= kMaxDevices) return PA_ERR_LAUNCH;
+    void *ws = nullptr;
+    if (scratch_on(device, &ws) != hipSuccess) return PA_ERR_LAUNCH;
+    // every kernel writes each workspace piece before anything reads it, so
+    // the scratch needs no clearing between calls
+    return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
+                     max_context_len, scale, partition, ws, (size_t)PA_NOALLOC_SCRATCH_BYTES,
+                     dtype, algo, stream);
 }
 
 }  // extern "C"

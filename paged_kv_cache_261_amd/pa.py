@@ -19,7 +19,9 @@ PA_F32, PA_BF16 = 0, 1
 PA_ALGO_AUTO, PA_ALGO_VECTOR, PA_ALGO_MFMA = 0, 1, 2
 PA_PARTITION_AUTO, PA_PARTITION_BALANCED, PA_PARTITION_SHARED = -1, -2, -3
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
-          -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALGO", -7: "PA_ERR_ALIGN"}
+          -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALGO", -7: "PA_ERR_ALIGN",
+          -8: "PA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES
 
 
 class PAError(RuntimeError):
@@ -43,6 +45,7 @@ def _load():
         "pa_decode": (I, [P] * 6 + [I] * 8 + [F, I, P, SZ, I, I, P]),
         "pa_decode_partitions": (I, [P] * 6 + [I] * 8 + [F, I, P, SZ, I, I, P]),
         "pa_decode_reduce": (I, [P, P, I, I, I, I, I, I, P, SZ, I, P]),
+        "pa_decode_noalloc": (I, [P] * 6 + [I] * 8 + [F, I, I, I, P]),
         "pa_status_string": (C.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
@@ -213,3 +216,12 @@ def pa_decode_reduce(out, context_lens, num_kv_heads, max_context_len, partition
                                 int(num_kv_heads), d, int(max_context_len), int(partition_size),
                                 ws, wsb, dtype_code(out), _stream(out, stream)),
            "pa_decode_reduce")
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      max_context_len, partition_size=-1, algo=PA_ALGO_AUTO, stream=None):
+    """pa_decode without a workspace argument: split modes use the library's
+    static per-GPU scratch, so the call allocates nothing."""
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len)
+    _check(lib.pa_decode_noalloc(*args, float(scale), int(partition_size), dtype_code(q),
+                                 int(algo), _stream(q, stream)), "pa_decode_noalloc")
