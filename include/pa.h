@@ -168,6 +168,19 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
                int max_context_len, int max_q_len, float scale, int dtype, void *stream);
 
 /*
+ * Split-context decode, the common source of the next four calls.  The one
+ * softmax over a whole context of "CS349E 第 7 讲 01_paged_attention.py"
+ * (demo 2, paper eq. 4: scores block by block, one softmax over all blocks,
+ * V multiplied in block by block) does not depend on how the blocks are
+ * grouped: a group of blocks keeps its own max m, its sum
+ * l = sum 2^(s - m) and its weighted V sum acc, and groups combine by
+ * rescaling each by 2^(m - M), M the largest m.  Splitting a long context
+ * into such groups lets many wavefronts share one sequence.  The pages name
+ * no split: "04 - Paged Attention 实现进度" (section A.3) names a second
+ * generation of vLLM's kernel (v2) only by its tiling.
+ */
+
+/*
  * Partition mode the library uses when pa_decode / pa_decode_partitions get
  * partition_size == PA_PARTITION_AUTO for these sizes and PA_ALGO_AUTO:
  * 0 (single pass, no workspace), PA_PARTITION_BALANCED, or a multiple of
@@ -185,10 +198,14 @@ int pa_decode_auto_partition(int num_seqs, int num_q_heads, int num_kv_heads, in
                              int block_size, int max_context_len, int dtype);
 
 /*
- * Bytes of device workspace pa_decode needs (0 in single-pass mode).
- * partition_size as for pa_decode; for PA_PARTITION_AUTO the size is enough
- * for every mode the library may pick for these sizes.  Returns 0 for
- * invalid sizes as well.
+ * Bytes of device workspace pa_decode needs (0 in single-pass mode): the
+ * (m, l, acc) states of the groups of a split context (above), plus, in the
+ * balanced and shared modes, the plan that splits the work.  partition_size
+ * as for pa_decode; for PA_PARTITION_AUTO the size is enough for every mode
+ * the library may pick for these sizes.  dtype selects the kernel the mode
+ * runs on (and so whether the mode applies); num_kv_heads and block_size
+ * likewise.  A pure host function: no device call.  Returns 0 for invalid
+ * sizes, and for modes the shape cannot run, as well.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                 int block_size, int max_context_len, int partition_size,
@@ -256,7 +273,8 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
               void *workspace, size_t workspace_bytes, int dtype, int algo, void *stream);
 
 /*
- * Phase 1 of split-context decode: per (sequence, query head, partition p)
+ * Phase 1 of split-context decode (the grouping above): per (sequence, query
+ * head, partition p)
  * of partition_size tokens (a positive multiple of block_size), the running
  * max m_p (base-2 log domain: scores times scale*log2(e)), the sum
  * l_p = sum_j 2^(s_j - m_p) and the unnormalised acc_p = sum_j 2^(s_j - m_p)
@@ -281,15 +299,17 @@ int pa_decode_partitions(void *out, const void *q, const void *k_cache, const vo
                          void *stream);
 
 /*
- * Phase 2 of split-context decode: for every sequence with more than one
- * partition, merge the partitions in ascending order:
+ * Phase 2 of split-context decode (the combination rule above): for every
+ * sequence with more than one partition, merge the partitions in ascending
+ * order:
  *     M = max_p m_p,  w_p = 2^(m_p - M),
  *     out = (sum_p w_p acc_p) / (sum_p w_p l_p).
- * Sequences with one partition are left alone (phase 1 wrote them).
- * partition_size must be the value phase 1 resolved (not PA_PARTITION_AUTO;
- * see pa_decode_auto_partition); with PA_PARTITION_BALANCED the pieces of
- * each (sequence, KV head) are merged the same way, and empty contexts get
- * zeros.
+ * Sequences with one partition are left alone (phase 1 wrote them);
+ * empty contexts get zeros here.  partition_size must be the value phase 1
+ * resolved (not PA_PARTITION_AUTO; see pa_decode_auto_partition); with
+ * PA_PARTITION_BALANCED or PA_PARTITION_SHARED the pieces of each
+ * (sequence, KV head) are merged the same way, and empty contexts get zeros
+ * too.
  */
 int pa_decode_reduce(void *out, const int32_t *context_lens, int num_seqs, int num_q_heads,
                      int num_kv_heads, int head_dim, int max_context_len, int partition_size,
@@ -325,7 +345,13 @@ int pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void 
                       int block_size, int max_blocks_per_seq, int max_context_len, float scale,
                       int partition_size, int dtype, int algo, void *stream);
 
-/* A static, human-readable name for a status code. */
+/*
+ * A static, human-readable name for a status code.  Every entry point
+ * reports failure by its return value instead of aborting, as
+ * "PagedAttention实现" (PagedKVManager::allocate_block) returns false when
+ * no free block is left; this turns the code into text.  Never NULL;
+ * unknown codes give "unknown status".
+ */
 const char *pa_status_string(int status);
 
 #ifdef __cplusplus
