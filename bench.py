@@ -19,9 +19,14 @@ step (logical KV bytes the step's queries read / step time, in GB/s);
 layer).  `roofline` prices the dominant kernel (the decode kernel) against
 MI355X's 8 TB/s HBM peak with its algorithmic bytes (unique KV blocks + q +
 out + block tables + context lengths) over its average duration, measured
-with HIP events on the launch stream.  `cpu_baseline` times the CPU oracle
-(float64 concatenate-then-attend plus the slot write) on a bounded sample of
-the same workload on this host's cores.
+with HIP events on the launch stream.  With the default workload the same
+line also carries, under `workloads`, the two other bf16 GQA decode
+workloads (shared-prefix sampling and long-context split decode), each timed
+the same way with its own roofline, and `stream_read`, the rate of a plain
+streaming read of a 2 GiB buffer on the same GPU (context for the roofline).
+`cpu_baseline` times the CPU oracle (float64 concatenate-then-attend plus
+the slot write) on a bounded sample of the headline workload on this host's
+cores.
 """
 from __future__ import annotations
 
@@ -154,12 +159,36 @@ class BeamLastStep:
         return self.bw.kv_unique_bytes(len(self.bw.steps) - 1)
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads():
+    """Threads for the oracle baseline: every core this process may run on,
+    but no more than the host's CPU share for one GPU where the environment
+    states it (OMP_NUM_THREADS)."""
+    n = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
+
+
 def cpu_baseline(w, target_seconds):
     """Time the oracle (slot write of the step's tokens + float64
-    concatenate-then-attend) on a bounded prefix of the batch, all cores."""
+    concatenate-then-attend) on a bounded prefix of the batch, on every
+    thread cpu_threads() allows and on one thread."""
     from oracle import pao
     c = w.cfg
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    cores = cpu_threads()
     kh = np.zeros((c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim),
                   dtype=w.prefill_k.dtype)
     vh = np.zeros_like(kh)
@@ -184,8 +213,8 @@ def cpu_baseline(w, target_seconds):
     def kv_bytes(n):
         return int(ctx[:n].astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * es
 
-    # all cores: grow the prefix until one run takes a quarter of the budget
-    # (or the batch is whole), then repeat it within the budget; median
+    # all threads: grow the prefix until one run takes a quarter of the
+    # budget (or the batch is whole), then repeat it within the budget; median
     n = min(c.num_seqs, max(1, cores))
     dt = run(n, cores)
     while n < c.num_seqs and dt < target_seconds / 4:
@@ -195,7 +224,7 @@ def cpu_baseline(w, target_seconds):
     while sum(times) < target_seconds and len(times) < 40:
         times.append(run(n, cores))
     dt = statistics.median(times)
-    # one core, on a prefix about 1/cores as long
+    # one thread, on a prefix about 1/cores as long
     n1 = max(1, n // cores)
     t1 = run(n1, 1)
     return {"value": round(kv_bytes(n) / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
@@ -203,6 +232,10 @@ def cpu_baseline(w, target_seconds):
             "sample": f"first {n} of {c.num_seqs} sequences of {c.name} "
                       f"(sum ctx {int(ctx[:n].sum())}), one step, median of {len(times)} "
                       f"runs, {dt:.3f} s each",
+            "cpu_model": cpu_model(),
+            "cores_available": len(os.sched_getaffinity(0)),
+            "threads_rule": "every core in the process's affinity mask, capped by "
+                            "OMP_NUM_THREADS (the host's CPU share per GPU) where set",
             "tokens_per_s": round(n / dt, 3),
             "single_thread": {"value": round(kv_bytes(n1) / t1 / 1e9, 4), "unit": "GB/s",
                               "sample": f"first {n1} sequences, {t1:.3f} s"}}
@@ -282,6 +315,252 @@ def bench_prefill(args, torch, pa, S, dev):
     print(json.dumps(result), flush=True)
 
 
+class DecodeRun:
+    """One decode workload resident on the GPU: pools built through the slot
+    write, the step's inputs, the workspace of its split mode, and the step
+    itself (copy-on-write copies where the workload has them, the slot
+    write, decode phase 1 and the merge)."""
+
+    def __init__(self, w, torch, pa, dev, algo, algo_name, part_req):
+        self.w, self.torch, self.pa, self.algo, self.algo_name = w, torch, pa, algo, algo_name
+        c = self.c = w.cfg
+        tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+
+        def dev_t(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        self.dev_t = dev_t
+        shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+        self.k_cache = torch.zeros(shape, dtype=tdt, device=dev)
+        self.v_cache = torch.zeros(shape, dtype=tdt, device=dev)
+        pa.pa_reshape_and_cache(dev_t(w.prefill_k), dev_t(w.prefill_v), self.k_cache,
+                                self.v_cache, dev_t(w.prefill_slots))
+        for st in getattr(w, "earlier_steps", []):   # beam workloads: steps before the last
+            if len(st.cow):
+                pa.pa_copy_blocks(self.k_cache, self.v_cache, dev_t(st.cow))
+            pa.pa_reshape_and_cache(dev_t(st.k), dev_t(st.v), self.k_cache, self.v_cache,
+                                    dev_t(st.slots))
+        cow_h = getattr(w, "cow", np.zeros((0, 2), dtype=np.int32))
+        self.cow = dev_t(cow_h) if len(cow_h) else None
+        self.q = dev_t(w.q[0])
+        self.new_k, self.new_v = dev_t(w.step_k[0]), dev_t(w.step_v[0])
+        self.slots = dev_t(w.step_slots[0])
+        self.ctx_h = w.ctx_at(0)
+        self.tables = dev_t(w.tables_at(0))
+        self.ctx = dev_t(self.ctx_h)
+        self.max_ctx = int(self.ctx_h.max())
+        self.out = torch.empty_like(self.q)
+        part = (pa.pa_decode_auto_partition(c.num_seqs, c.num_q_heads, c.num_kv_heads,
+                                            c.head_dim, c.block_size, self.max_ctx,
+                                            pa.dtype_code(self.q))
+                if part_req == -1 else part_req)
+        if part == pa.PA_PARTITION_BALANCED and algo_name == "vector" and c.dtype == "bf16" \
+                and c.head_dim < 32:
+            part = 512
+        self.part = part
+        self.ws = pa.workspace_for(self.q, self.k_cache, self.max_ctx, part)
+        torch.cuda.synchronize()
+
+    def decode(self, stream, evs=None):
+        """The decode phase: phase 1 (evs[0] after it) and the merge."""
+        pa, c = self.pa, self.c
+        if self.part == 0:
+            pa.pa_decode(self.out, self.q, self.k_cache, self.v_cache, self.tables, self.ctx,
+                         c.scale, self.max_ctx, 0, None, self.algo, stream=stream)
+            if evs is not None:
+                evs[0].record(stream)
+            return
+        pa.pa_decode_partitions(self.out, self.q, self.k_cache, self.v_cache, self.tables,
+                                self.ctx, c.scale, self.max_ctx, self.part, self.ws, self.algo,
+                                stream=stream)
+        if evs is not None:
+            evs[0].record(stream)
+        pa.pa_decode_reduce(self.out, self.ctx, c.num_kv_heads, self.max_ctx, self.part,
+                            self.ws, stream=stream)
+
+    def step(self, stream, evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        if self.cow is not None:    # the step's copy-on-write copies, then its writes
+            self.pa.pa_copy_blocks(self.k_cache, self.v_cache, self.cow, stream=stream)
+        self.pa.pa_reshape_and_cache(self.new_k, self.new_v, self.k_cache, self.v_cache,
+                                     self.slots, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        self.decode(stream, None if evs is None else evs[2:3])
+        if evs is not None:
+            evs[3].record(stream)
+
+    def time(self, steps, warmup):
+        """Wall clock over exactly `steps` steps after `warmup`, then per-phase
+        HIP-event durations on the launch stream and the decode phase with
+        cold caches."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            self.step(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for e in evs:
+            self.step(stream, e)
+        torch.cuda.synchronize()
+        t_write = [e[0].elapsed_time(e[1]) for e in evs]
+        t_main = [e[1].elapsed_time(e[2]) for e in evs]
+        t_reduce = [e[2].elapsed_time(e[3]) for e in evs]
+        t_step = [e[0].elapsed_time(e[3]) for e in evs]
+        # cold caches: reading a 1 GiB buffer between launches evicts L2 and
+        # the MALL (not timed; a read leaves no dirty lines to write back)
+        flush = torch.ones(1 << 27, dtype=torch.int64, device=self.q.device)
+        cold = []
+        for _ in range(min(steps, 20)):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            self.decode(stream, [e1])
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del flush
+        return {"wall_ms": wall * 1e3, "write": t_write, "main": t_main, "reduce": t_reduce,
+                "step": t_step, "cold": cold}
+
+    def bytes(self):
+        c, w, ctx_h = self.c, self.w, self.ctx_h
+        es = 2 if c.dtype == "bf16" else 4
+        kv_logical = w.kv_logical_bytes(0)
+        kv_unique = w.kv_unique_bytes(0)
+        qo = 2 * c.num_seqs * c.num_q_heads * c.head_dim * es
+        tables = int(((ctx_h + c.block_size - 1) // c.block_size).sum()) * 4 + 4 * c.num_seqs
+        return {"kv_logical": kv_logical, "kv_unique": kv_unique,
+                "decode_algorithmic": kv_unique + qo + tables}
+
+    def free(self):
+        for name in ("k_cache", "v_cache", "q", "out", "ws", "tables", "ctx", "new_k", "new_v",
+                     "slots", "cow"):
+            setattr(self, name, None)
+        self.torch.cuda.empty_cache()
+
+
+def decode_record(run, t, steps, args):
+    """The numbers of one timed decode workload (shared by the headline and
+    the extra workloads)."""
+    c = run.c
+    by = run.bytes()
+    ms_step = t["wall_ms"] / steps
+    main_ms = statistics.mean(t["main"])
+    red_ms = statistics.mean(t["reduce"])
+    alg = by["decode_algorithmic"]
+    achieved = alg / (main_ms * 1e-3) / 1e9
+    with_merge = alg / ((main_ms + red_ms) * 1e-3) / 1e9
+    shared = run.part == -3
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac_with_merge": round(with_merge / HBM_PEAK_GBS, 4),
+            "kernel": decode_kernel_name(c, run.part, run.algo_name),
+            "bytes_per_launch": alg,
+            "time": "plan + decode kernels (merge in frac_with_merge)" if shared
+                    else "decode kernel (merge in frac_with_merge)"}
+    traffic = load_traffic(c.name, run.algo_name, run.part)
+    roof["traffic"] = traffic
+    roof["traffic_source"] = ("rocprofv3 FETCH_SIZE/WRITE_SIZE per launch, committed in "
+                              "profiles/traffic.json and taken on kernel sources that hash the "
+                              "same as these" if traffic is not None else
+                              "none: no counter run on the current kernel sources")
+    return {
+        "value": round(by["kv_logical"] / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "ms_per_step": round(ms_step, 5),
+        "config": {"workload": c.name, "description": c.description, "batch": c.num_seqs,
+                   "num_q_heads": c.num_q_heads, "num_kv_heads": c.num_kv_heads,
+                   "head_dim": c.head_dim, "block_size": c.block_size,
+                   "sum_context": int(run.ctx_h.sum()), "max_context": run.max_ctx,
+                   "partition_size": run.part, "algo": run.algo_name,
+                   "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(c.num_seqs / (ms_step * 1e-3), 1),
+        "hbm_peak_frac_step": round(by["kv_logical"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    4),
+        "kernels_ms": {"reshape_and_cache": round(statistics.mean(t["write"]), 5),
+                       "decode": round(main_ms, 5), "reduce": round(red_ms, 5),
+                       "step_events": round(statistics.mean(t["step"]), 5),
+                       "decode_cold_l2": round(statistics.median(t["cold"]), 5),
+                       "decode_p10": round(float(np.percentile(t["main"], 10)), 5),
+                       "decode_p90": round(float(np.percentile(t["main"], 90)), 5)},
+        "bytes": by,
+        "roofline": roof,
+    }
+
+
+def bench_copy_blocks(run, torch):
+    """pa_copy_blocks on up to 4096 pairs, each from a block the tables use
+    into one they do not (the decode inputs stay intact)."""
+    c, pa = run.c, run.pa
+    stream = torch.cuda.current_stream()
+    used = np.unique(run.w.tables_at(0)[run.w.tables_at(0) >= 0])
+    free_blocks = np.setdiff1d(np.arange(c.num_blocks), used)
+    rng = np.random.default_rng(1234)
+    n_cp = int(min(4096, len(free_blocks)))
+    if n_cp == 0:
+        return None
+    pairs = np.stack([rng.choice(used, size=n_cp), rng.permutation(free_blocks)[:n_cp]],
+                     axis=1).astype(np.int32)
+    pairs_d = run.dev_t(pairs)
+    for _ in range(3):
+        pa.pa_copy_blocks(run.k_cache, run.v_cache, pairs_d, stream=stream)
+    cp_ms = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pa.pa_copy_blocks(run.k_cache, run.v_cache, pairs_d, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cp_ms.append(e0.elapsed_time(e1))
+    block_bytes = c.num_kv_heads * c.block_size * c.head_dim * (2 if c.dtype == "bf16" else 4)
+    cp_bytes = 4 * n_cp * block_bytes                 # read + write, K and V
+    cp_t = statistics.median(cp_ms)
+    return {"pairs": n_cp, "ms": round(cp_t, 5), "bytes": cp_bytes,
+            "GBs": round(cp_bytes / (cp_t * 1e-3) / 1e9, 1),
+            "frac": round(cp_bytes / (cp_t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel": "copy_blocks_kernel"}
+
+
+def bench_stream_read(torch, pa, dev):
+    """A plain streaming read of a 2 GiB buffer (the calibration kernel of
+    libpa.so), with the non-temporal hint the decode kernels use and with the
+    default policy: the practical read ceiling of this GPU, as context."""
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(pa.MEASURE_SINK_WORDS, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    rec = {"bytes": nbytes, "kernel": "stream_read_kernel", "runs": 20}
+    for nt in (True, False):
+        for _ in range(3):
+            pa.pa_measure_stream_read(buf, sink, nontemporal=nt, stream=stream)
+        ms = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pa.pa_measure_stream_read(buf, sink, nontemporal=nt, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        rec["nontemporal_GBs" if nt else "default_GBs"] = round(
+            nbytes / (statistics.median(ms) * 1e-3) / 1e9, 1)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return rec
+
+
+# The other bf16 GQA decode workloads, timed in the same run as the default
+# one (each with its own launch configuration and roofline).
+EXTRA_WORKLOADS = ["shared_prefix_bf16", "long_split_bf16"]
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -304,194 +583,51 @@ def main():
 
     if args.config in S.PREFILL_CONFIGS:
         return bench_prefill(args, torch, pa, S, dev)
+
+    def make(name):
+        return BeamLastStep(S.make_beam_workload(name)) if name in S.BEAM_CONFIGS \
+            else S.make_workload(name)
+
     log(f"building workload {args.config}")
-    w = BeamLastStep(S.make_beam_workload(args.config)) if args.config in S.BEAM_CONFIGS \
-        else S.make_workload(args.config)
-    c = w.cfg
-    tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    w = make(args.config)
+    part_req = w.cfg.partition_size if args.partition is None else args.partition
+    run = DecodeRun(w, torch, pa, dev, algo, args.algo, part_req)
+    log(f"workload ready: batch {w.cfg.num_seqs}, sum ctx {int(run.ctx_h.sum())}, "
+        f"partition {run.part}, algo {args.algo}")
+    t = run.time(args.steps, args.warmup)
+    log(f"timed {args.steps} steps: {t['wall_ms']:.2f} ms")
+    rec = decode_record(run, t, args.steps, args)
+    copy_rec = bench_copy_blocks(run, torch)
+    run.free()
 
-    def dev_t(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
+    result = {"metric": METRIC, "value": rec["value"], "unit": "GB/s", "n_gpus": 1,
+              "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": w.cfg.dtype, "data": "synthetic"}
+    for key in ("config", "tokens_per_s", "hbm_peak_frac_step", "kernels_ms", "bytes",
+                "roofline"):
+        result[key] = rec[key]
+    result["copy_blocks"] = copy_rec
 
-    shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
-    k_cache = torch.zeros(shape, dtype=tdt, device=dev)
-    v_cache = torch.zeros(shape, dtype=tdt, device=dev)
-    pa.pa_reshape_and_cache(dev_t(w.prefill_k), dev_t(w.prefill_v), k_cache, v_cache,
-                            dev_t(w.prefill_slots))
-    for st in getattr(w, "earlier_steps", []):   # beam workloads: the steps before the last
-        if len(st.cow):
-            pa.pa_copy_blocks(k_cache, v_cache, dev_t(st.cow))
-        pa.pa_reshape_and_cache(dev_t(st.k), dev_t(st.v), k_cache, v_cache, dev_t(st.slots))
-    cow_h = getattr(w, "cow", np.zeros((0, 2), dtype=np.int32))
-    cow = dev_t(cow_h) if len(cow_h) else None
-    q = dev_t(w.q[0])
-    new_k, new_v = dev_t(w.step_k[0]), dev_t(w.step_v[0])
-    slots = dev_t(w.step_slots[0])
-    ctx_h = w.ctx_at(0)
-    tables = dev_t(w.tables_at(0))
-    ctx = dev_t(ctx_h)
-    max_ctx = int(ctx_h.max())
-    out = torch.empty_like(q)
-    part_req = c.partition_size if args.partition is None else args.partition
-    part = (pa.pa_decode_auto_partition(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                                        c.block_size, max_ctx, pa.dtype_code(q))
-            if part_req == -1 else part_req)
-    if part == pa.PA_PARTITION_BALANCED and args.algo == "vector":
-        part = 512
-    ws = pa.workspace_for(q, k_cache, max_ctx, part)
-    torch.cuda.synchronize()
-    log(f"workload ready: batch {c.num_seqs}, sum ctx {int(ctx_h.sum())}, partition {part}, "
-        f"algo {args.algo}")
-
-    stream = torch.cuda.current_stream()
-
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record(stream)
-        if cow is not None:         # the step's copy-on-write copies, then its writes
-            pa.pa_copy_blocks(k_cache, v_cache, cow, stream=stream)
-        pa.pa_reshape_and_cache(new_k, new_v, k_cache, v_cache, slots, stream=stream)
-        if evs is not None:
-            evs[1].record(stream)
-        if part == 0:
-            pa.pa_decode(out, q, k_cache, v_cache, tables, ctx, c.scale, max_ctx, 0, None, algo,
-                         stream=stream)
-            if evs is not None:
-                evs[2].record(stream)
-                evs[3].record(stream)
-        else:
-            pa.pa_decode_partitions(out, q, k_cache, v_cache, tables, ctx, c.scale, max_ctx, part,
-                                    ws, algo, stream=stream)
-            if evs is not None:
-                evs[2].record(stream)
-            pa.pa_decode_reduce(out, ctx, c.num_kv_heads, max_ctx, part, ws, stream=stream)
-            if evs is not None:
-                evs[3].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # (1) wall clock over exactly K steps
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    log(f"timed {args.steps} steps: {wall * 1e3:.2f} ms")
-
-    # (2) per-kernel durations with HIP events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for e in evs:
-        step(e)
-    torch.cuda.synchronize()
-    t_write = [e[0].elapsed_time(e[1]) for e in evs]
-    t_main = [e[1].elapsed_time(e[2]) for e in evs]
-    t_reduce = [e[2].elapsed_time(e[3]) for e in evs]
-    t_step = [e[0].elapsed_time(e[3]) for e in evs]
-
-    # (4) copy-on-write block copies (pa_copy_blocks): up to 4096 pairs, each
-    # from a block the tables use into one they do not (the decode inputs
-    # stay intact)
-    used = np.unique(w.tables_at(0)[w.tables_at(0) >= 0])
-    free_blocks = np.setdiff1d(np.arange(c.num_blocks), used)
-    rng = np.random.default_rng(1234)
-    n_cp = int(min(4096, len(free_blocks)))
-    copy_rec = None
-    if n_cp > 0:
-        pairs = np.stack([rng.choice(used, size=n_cp), rng.permutation(free_blocks)[:n_cp]],
-                         axis=1).astype(np.int32)
-        pairs_d = dev_t(pairs)
-        for _ in range(3):
-            pa.pa_copy_blocks(k_cache, v_cache, pairs_d, stream=stream)
-        cp_ms = []
-        for _ in range(20):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            pa.pa_copy_blocks(k_cache, v_cache, pairs_d, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            cp_ms.append(e0.elapsed_time(e1))
-        block_bytes = c.num_kv_heads * c.block_size * c.head_dim * (2 if c.dtype == "bf16" else 4)
-        cp_bytes = 4 * n_cp * block_bytes                 # read + write, K and V
-        cp_t = statistics.median(cp_ms)
-        copy_rec = {"pairs": n_cp, "ms": round(cp_t, 5), "bytes": cp_bytes,
-                    "GBs": round(cp_bytes / (cp_t * 1e-3) / 1e9, 1),
-                    "frac": round(cp_bytes / (cp_t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                    "kernel": "copy_blocks_kernel"}
-
-    es = 2 if c.dtype == "bf16" else 4
-    kv_logical = w.kv_logical_bytes(0)
-    kv_unique = w.kv_unique_bytes(0)
-    qo_bytes = 2 * c.num_seqs * c.num_q_heads * c.head_dim * es
-    table_bytes = int(((ctx_h + c.block_size - 1) // c.block_size).sum()) * 4 + 4 * c.num_seqs
-    decode_alg = kv_unique + qo_bytes + table_bytes
-    ms_step = wall / args.steps * 1e3
-    main_ms = statistics.mean(t_main)
-    achieved = decode_alg / (main_ms * 1e-3) / 1e9
-    algo_name = args.algo
-    traffic = load_traffic(args.config, algo_name, part)
-    kernel_name = decode_kernel_name(c, part, args.algo)
-
-    # (3) the decode phase with caches cold: reading a 1 GiB buffer between
-    # launches evicts L2 and the MALL (not timed; a read leaves no dirty
-    # lines to write back during the decode)
-    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)
-    cold = []
-    for _ in range(min(args.steps, 20)):
-        flush.sum()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        if part == 0:
-            pa.pa_decode(out, q, k_cache, v_cache, tables, ctx, c.scale, max_ctx, 0, None, algo,
-                         stream=stream)
-        else:
-            pa.pa_decode_partitions(out, q, k_cache, v_cache, tables, ctx, c.scale, max_ctx, part,
-                                    ws, algo, stream=stream)
-        e1.record(stream)
-        if part != 0:
-            pa.pa_decode_reduce(out, ctx, c.num_kv_heads, max_ctx, part, ws, stream=stream)
-        torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
-    del flush
-
-    result = {
-        "metric": METRIC,
-        "value": round(kv_logical / (ms_step * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": c.dtype,
-        "data": "synthetic",
-        "config": {"workload": c.name, "description": c.description, "batch": c.num_seqs,
-                   "num_q_heads": c.num_q_heads, "num_kv_heads": c.num_kv_heads,
-                   "head_dim": c.head_dim, "block_size": c.block_size,
-                   "sum_context": int(ctx_h.sum()), "max_context": max_ctx,
-                   "partition_size": part, "algo": algo_name, "parallelism": "none (1 GPU)"},
-        "tokens_per_s": round(c.num_seqs / (ms_step * 1e-3), 1),
-        "hbm_peak_frac_step": round(kv_logical / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "kernels_ms": {"reshape_and_cache": round(statistics.mean(t_write), 5),
-                       "decode": round(main_ms, 5),
-                       "reduce": round(statistics.mean(t_reduce), 5),
-                       "step_events": round(statistics.mean(t_step), 5),
-                       "decode_cold_l2": round(statistics.median(cold), 5),
-                       "decode_p10": round(float(np.percentile(t_main, 10)), 5),
-                       "decode_p90": round(float(np.percentile(t_main, 90)), 5)},
-        "bytes": {"kv_logical": kv_logical, "kv_unique": kv_unique,
-                  "decode_algorithmic": decode_alg},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": kernel_name},
-        "copy_blocks": copy_rec,
-    }
+    default_run = args.config == DEFAULT_CONFIG and args.partition is None and \
+        args.algo == "auto"
+    if default_run:
+        result["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            log(f"building workload {name}")
+            wx = make(name)
+            rx = DecodeRun(wx, torch, pa, dev, algo, args.algo, wx.cfg.partition_size)
+            tx = rx.time(args.steps, args.warmup)
+            log(f"timed {args.steps} steps of {name}: {tx['wall_ms']:.2f} ms")
+            result["workloads"][name] = decode_record(rx, tx, args.steps, args)
+            rx.free()
+            del wx
+        log("streaming-read ceiling")
+        result["stream_read"] = bench_stream_read(torch, pa, dev)
+        nt = result["stream_read"]["nontemporal_GBs"]
+        result["roofline"]["frac_of_stream_read"] = round(result["roofline"]["achieved"] / nt, 4)
+        for r in result["workloads"].values():
+            r["roofline"]["frac_of_stream_read"] = round(r["roofline"]["achieved"] / nt, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -46,6 +46,7 @@ def _load():
         "pa_decode_partitions": (I, [P] * 6 + [I] * 8 + [F, I, P, SZ, I, I, P]),
         "pa_decode_reduce": (I, [P, P, I, I, I, I, I, I, P, SZ, I, P]),
         "pa_decode_noalloc": (I, [P] * 6 + [I] * 8 + [F, I, I, I, P]),
+        "pa_measure_stream_read": (I, [P, SZ, I, P, P]),
         "pa_status_string": (C.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
@@ -225,3 +226,17 @@ def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scal
     args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len)
     _check(lib.pa_decode_noalloc(*args, float(scale), int(partition_size), dtype_code(q),
                                  int(algo), _stream(q, stream)), "pa_decode_noalloc")
+
+
+MEASURE_SINK_WORDS = 4096   # PA_MEASURE_SINK_WORDS (include/pa_measure.h)
+
+
+def pa_measure_stream_read(buf, sink, nontemporal=True, stream=None):
+    """Calibration only: read every byte of the device tensor `buf` once (the
+    benchmark's streaming-read ceiling); sink is an int32 device tensor of
+    MEASURE_SINK_WORDS words whose XOR equals the XOR of buf's 32-bit words."""
+    if sink.dtype != torch.int32 or sink.numel() < MEASURE_SINK_WORDS:
+        raise ValueError("sink must be an int32 tensor of MEASURE_SINK_WORDS words")
+    _check(lib.pa_measure_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                      1 if nontemporal else 0, _dev(sink, "sink"),
+                                      _stream(buf, stream)), "pa_measure_stream_read")

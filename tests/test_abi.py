@@ -8,15 +8,20 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa.h")
+INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(ROOT, "paged_kv_cache_261_amd", "libpa.so")
 
 OK, NULL, SHAPE, UNSUP, WS, LAUNCH, ALGO, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|size_t|const char \*)\s*(pa_\w+)\(", text, re.M)))
+    """Every function the headers under include/ declare."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            names |= set(re.findall(r"^(?:int|size_t|const char \*)\s*(pa_\w+)\(", text, re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -33,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) >= {"pa_reshape_and_cache", "pa_decode", "pa_decode_partitions",
                           "pa_decode_reduce", "pa_decode_workspace_size",
                           "pa_decode_auto_partition", "pa_status_string", "pa_copy_blocks",
-                          "pa_prefill", "pa_decode_noalloc"}
+                          "pa_prefill", "pa_decode_noalloc", "pa_measure_stream_read"}
     raw = C.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), n
@@ -145,6 +150,14 @@ SCRATCH = -8
 def test_noalloc_rejects_bad_arguments_and_oversized_problems(lib, kw, status):
     """Host validation and the scratch bound come before any HIP call."""
     assert noalloc_call(lib, **kw) == status
+
+
+@needs_no_gpu
+def test_stream_read_rejects_bad_arguments(lib):
+    assert lib.pa_measure_stream_read(Z, 1 << 20, 1, A, Z) == NULL
+    assert lib.pa_measure_stream_read(A, 1 << 20, 1, Z, Z) == NULL
+    assert lib.pa_measure_stream_read(MIS, 1 << 20, 1, A, Z) == ALIGN
+    assert lib.pa_measure_stream_read(A, (1 << 20) + 8, 0, A, Z) == ALIGN
 
 
 @needs_no_gpu

@@ -134,15 +134,27 @@ def test_small_workloads_whole(name):
         for algo, part in modes_for(w.cfg):
             got = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, w.max_context_len, part, algo)
             H.assert_close_to_oracle(got, ref, w.cfg.dtype, f"{name} step {step} algo {algo} "
-                                                            f"partition {part}")
+                                                            f"partition {part}",
+                                     report=step == 0 and algo == AUTO and part == -1)
+
+
+@functools.lru_cache(maxsize=1)
+def full_ref(name):
+    """The oracle's float64 result for every row of a full-size workload."""
+    w, kd, vd, kh, vh = full(name)
+    note(f"[gpu parity] oracle over every row of {name}")
+    return pao.decode_concat(w.q[0], kh, vh, w.tables_at(0), w.ctx_at(0), w.cfg.scale)
 
 
 @pytest.mark.parametrize("name", ["gqa_bf16", "shared_prefix_bf16", "long_split_bf16"])
-def test_full_size_sampled(name):
+def test_full_size_every_row(name):
+    """Every (sequence, head) row of the three bf16 workloads at full size
+    against the oracle, in the launch configuration the benchmark times
+    (the workload's split mode, PA_ALGO_AUTO), in the library's own choice
+    of mode, and in every other mode and kernel the shape admits."""
     w, kd, vd, kh, vh = full(name)
+    ref = full_ref(name)
     ctx, tab, q = w.ctx_at(0), w.tables_at(0), w.q[0]
-    idx = sample_seqs(w, 4 if name == "long_split_bf16" else 8)
-    ref = pao.decode_concat(q[idx], kh, vh, tab[idx], ctx[idx], w.cfg.scale)
     mc = int(ctx.max())
     bench_part = w.cfg.partition_size        # the launch configuration the benchmark times
     BAL, SHR = pa.PA_PARTITION_BALANCED, pa.PA_PARTITION_SHARED
@@ -150,21 +162,8 @@ def test_full_size_sampled(name):
                        (MFMA, 512), (VECTOR, 512), (MFMA, 256), (VECTOR, BAL)]:
         note(f"[gpu parity] {name} algo {algo} partition {part}")
         got = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, mc, part, algo)
-        H.assert_close_to_oracle(got[idx], ref, "bf16", f"{name} algo {algo} partition {part}")
-
-
-def test_full_size_all_rows_agree_across_modes():
-    """At full size, every row (not only the sampled ones) of the split and
-    single-pass matrix-core results and of the vector kernel agree within the
-    bf16 tolerance; rows sampled above pin them to the oracle."""
-    w, kd, vd, kh, vh = full("gqa_bf16")
-    ctx, tab, q = w.ctx_at(0), w.tables_at(0), w.q[0]
-    a = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, None, 512, MFMA)
-    b = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, None, 0, MFMA)
-    c = H.gpu_decode(q, kd, vd, tab, ctx, w.cfg.scale, None, 512, VECTOR)
-    assert np.isfinite(a).all()
-    assert H.row_rel_err(b, a).max() <= 1e-2
-    assert H.row_rel_err(c, a).max() <= 1e-2
+        H.assert_close_to_oracle(got, ref, "bf16", f"{name} algo {algo} partition {part}",
+                                 report=(algo, part) in ((AUTO, bench_part), (AUTO, -1)))
 
 
 # --------------------------------------------------------------------------
@@ -642,24 +641,29 @@ def test_balanced_split_cuts_anywhere(ctxs, hkv, G, mode):
 
 
 def test_copy_on_write_variant_of_shared_prefix():
-    """Shared-prefix sampling with 2056-token prompts: the last prompt block
-    holds 8 of 16 tokens, so the first private token of 7 of the 8 samples
-    copies it ("PagedAttention实现" cow_write; lecture 7 demo 3: n - 1 copies).
-    The pool copy is made on the device by pa_copy_blocks; the pools must
-    stay bit-identical, the outputs must equal the unshared layout bit for bit
-    and match the oracle."""
-    n_prompts, n_samples, prompt, private = 4, 8, 2056, 40
+    """The shared-prefix workload's shape with 2056-token prompts: 32 prompts
+    x 8 samples, 512 private tokens each.  The last prompt block holds 8 of
+    16 tokens, so the first private token of 7 of a prompt's 8 samples copies
+    it ("PagedAttention实现" cow_write; lecture 7 demo 3: n - 1 copies), 224
+    in all.  The allocator is the oracle's pool; each step's copies go to the
+    device in one pa_copy_blocks call, its tokens in one slot write.  The
+    pools stay bit-identical, every row matches the oracle in every split
+    mode, and each mode's output equals, bit for bit, the output over the
+    same logical content with every sample holding private blocks."""
+    n_prompts, n_samples, prompt, private = 32, 8, 2056, 512
     hq, hkv, d, bs = 32, 8, 128, 16
     B = n_prompts * n_samples
     rng = np.random.default_rng(5)
-    nb = 4096
+    nb = 16384
     pool = Pool(nb, bs, free_order=rng.permutation(nb).astype(np.int32))
     cfg = S.Config(name="cow", seed=0, num_seqs=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
-                   block_size=bs, num_blocks=nb, max_blocks_per_seq=(prompt + private) // bs + 2,
-                   dtype="bf16", scale=1 / math.sqrt(d), description="")
+                   block_size=bs, num_blocks=nb,
+                   max_blocks_per_seq=(prompt + private + bs - 1) // bs, dtype="bf16",
+                   scale=1 / math.sqrt(d), description="")
     kh, vh = H.empty_pool(cfg)
     kd, vd = H.dev_empty_pool(cfg)
-    seqs, logical_k, logical_v = [], [], []
+    note("[gpu parity] copy-on-write variant: prompts")
+    seqs, prompt_k, prompt_v = [], [], []
     for p in range(n_prompts):
         lead = pool.seq_new()
         pk = S._normal(rng, (prompt, hkv, d), "bf16")
@@ -667,41 +671,60 @@ def test_copy_on_write_variant_of_shared_prefix():
         slots = np.array([pool.append(lead)[0] for _ in range(prompt)])
         pao.slot_write(kh, vh, pk, pv, slots, bs)
         H.dev_write(kd, vd, pk, pv, slots)
-        group = [lead] + [pool.fork(lead) for _ in range(n_samples - 1)]
-        for s in group:
-            seqs.append(s)
-            logical_k.append([pk])
-            logical_v.append([pv])
-    copies = 0
+        seqs += [lead] + [pool.fork(lead) for _ in range(n_samples - 1)]
+        prompt_k += [pk] * n_samples
+        prompt_v += [pv] * n_samples
+    note("[gpu parity] copy-on-write variant: private tokens")
+    priv_k = S._normal(rng, (private, B, hkv, d), "bf16")
+    priv_v = S._normal(rng, (private, B, hkv, d), "bf16")
+    copies_at = []
     for t in range(private):
-        for i, s in enumerate(seqs):
+        step_slots, pairs = [], []
+        for s in seqs:
             slot, src, dst = pool.append(s)
+            step_slots.append(slot)
             if src >= 0:
-                copies += 1
+                pairs.append((src, dst))
                 pao.copy_block(kh, vh, src, dst)
-                pa.pa_copy_blocks(kd, vd, H.to_dev(np.array([[src, dst]], dtype=np.int32)))
-            tk = S._normal(rng, (1, hkv, d), "bf16")
-            tv = S._normal(rng, (1, hkv, d), "bf16")
-            pao.slot_write(kh, vh, tk, tv, np.array([slot]), bs)
-            H.dev_write(kd, vd, tk, tv, np.array([slot]))
-            logical_k[i].append(tk)
-            logical_v[i].append(tv)
-    assert copies == n_prompts * (n_samples - 1) == pool.stats()["n_copies"]
+        if pairs:
+            copies_at.append((t, len(pairs)))
+            pa.pa_copy_blocks(kd, vd, H.to_dev(np.array(pairs, dtype=np.int32)))
+        pao.slot_write(kh, vh, priv_k[t], priv_v[t], np.array(step_slots), bs)
+        H.dev_write(kd, vd, priv_k[t], priv_v[t], np.array(step_slots))
+    assert copies_at == [(0, n_prompts * (n_samples - 1))] == [(0, 224)]
+    assert pool.stats()["n_copies"] == 224
+    torch.cuda.synchronize()
     np.testing.assert_array_equal(H.to_host(kd), kh)
+    np.testing.assert_array_equal(H.to_host(vd), vh)
     tab = np.stack([pool.table(s, cfg.max_blocks_per_seq) for s in seqs])
     ctx = np.array([pool.seq_len(s) for s in seqs], dtype=np.int32)
+    assert (ctx == prompt + private).all()
     q = S._normal(rng, (B, hq, d), "bf16")
     ref = pao.decode_concat(q, kh, vh, tab, ctx, cfg.scale)
-    got = H.gpu_decode(q, kd, vd, tab, ctx, cfg.scale, None, 512, MFMA)
-    H.assert_close_to_oracle(got, ref, "bf16", "copy-on-write variant")
-    for mode in (pa.PA_PARTITION_SHARED, pa.PA_PARTITION_BALANCED, 0):
-        other = H.gpu_decode(q, kd, vd, tab, ctx, cfg.scale, None, mode, MFMA)
-        H.assert_close_to_oracle(other, ref, "bf16", f"copy-on-write variant, mode {mode}")
-    kl = [np.concatenate(x) for x in logical_k]
-    vl = [np.concatenate(x) for x in logical_v]
-    kc2, vc2, tab2 = H.paginate(kl, vl, bs, B * cfg.max_blocks_per_seq, rng, "bf16")
-    got2 = H.gpu_decode(q, H.to_dev(kc2), H.to_dev(vc2), tab2, ctx, cfg.scale, None, 512, MFMA)
-    np.testing.assert_array_equal(got, got2)
+    # the same logical content with private blocks only
+    kl = [np.concatenate([prompt_k[i], priv_k[:, i]]) for i in range(B)]
+    vl = [np.concatenate([prompt_v[i], priv_v[:, i]]) for i in range(B)]
+    kc2, vc2, tab2 = H.paginate(kl, vl, bs, B * cfg.max_blocks_per_seq + 8, rng, "bf16")
+    del kl, vl
+    kd2, vd2 = H.to_dev(kc2), H.to_dev(vc2)
+    del kc2, vc2
+    for algo, mode in ((AUTO, pa.PA_PARTITION_SHARED), (MFMA, pa.PA_PARTITION_BALANCED),
+                       (MFMA, 512), (MFMA, 0), (AUTO, -1)):
+        note(f"[gpu parity] copy-on-write variant, algo {algo} mode {mode}")
+        got = H.gpu_decode(q, kd, vd, tab, ctx, cfg.scale, None, mode, algo)
+        H.assert_close_to_oracle(got, ref, "bf16", f"copy-on-write variant, mode {mode}",
+                                 report=mode == pa.PA_PARTITION_SHARED)
+        got2 = H.gpu_decode(q, kd2, vd2, tab2, ctx, cfg.scale, None, mode, algo)
+        if mode != pa.PA_PARTITION_SHARED:
+            np.testing.assert_array_equal(got, got2)
+        else:
+            # shared mode splits its stream of distinct tiles between
+            # wavefronts: with private blocks the stream is longer, the cut
+            # points move and the pieces merge in other places, so only the
+            # tolerance holds
+            H.assert_close_to_oracle(got2, ref, "bf16", "private layout, shared mode")
+    del kd, vd, kd2, vd2
+    torch.cuda.empty_cache()
 
 
 # --------------------------------------------------------------------------
