@@ -157,9 +157,11 @@ int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int
  *   block_tables, k_cache, v_cache   as for pa_decode
  *   max_q_len      an upper bound of every n_b (sizes the grid)
  *
- * Supported: dtype PA_BF16, head_dim 128, block_size >= 16, group size <= 16
- * (the matrix-core tile); other shapes return PA_ERR_UNSUPPORTED.  Rows
- * with n_b = 0 produce nothing.  Asynchronous on `stream`, no workspace.
+ * Supported: head_dim in {16, 32, 64, 128, 256}; block_size a power of two in
+ * [1, 256]; group size at most 16; dtype PA_F32 or PA_BF16.  bfloat16 with
+ * head_dim 128 and block_size >= 16 runs on the matrix cores, every other
+ * shape on the vector ALUs (float32 arithmetic either way).  Chunks with
+ * n_b = 0 produce nothing.  Asynchronous on `stream`, no workspace.
  */
 int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
                const int32_t *block_tables, const int32_t *cu_seqlens_q,

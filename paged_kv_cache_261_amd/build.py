@@ -21,7 +21,7 @@ OBJ_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["pa_api.cpp", "pa_cache_write.hip", "pa_decode_vector.hip", "pa_decode_mfma.hip",
            "pa_decode_shared.hip", "pa_reduce.hip", "pa_copy_blocks.hip",
-           "pa_prefill.hip", "pa_measure.hip"]
+           "pa_prefill.hip", "pa_prefill_vector.hip", "pa_measure.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

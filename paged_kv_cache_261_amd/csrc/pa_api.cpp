@@ -399,10 +399,11 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
         max_blocks_per_seq <= 0 || max_context_len < 0 || max_q_len < 0 ||
         num_q_heads % num_kv_heads)
         return PA_ERR_SHAPE;
-    if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || !block_size_ok(block_size))
+    if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || !block_size_ok(block_size) ||
+        num_q_heads / num_kv_heads > 16)
         return PA_ERR_UNSUPPORTED;
-    if (!balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads))
-        return PA_ERR_UNSUPPORTED;
+    // the matrix-core kernel where its tile applies, the vector ALUs elsewhere
+    const bool mfma = balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads);
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size ||
         max_q_len > max_context_len)
         return PA_ERR_SHAPE;
@@ -427,14 +428,17 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
     p.log2_block = ilog2(block_size);
     p.max_blocks_per_seq = max_blocks_per_seq;
     p.max_context_len = max_context_len;
-    const int rows_per_wave = pa::kPrefillColumns / p.group;
+    const int rows_per_wave = mfma ? pa::kPrefillColumns / p.group
+                                   : pa::prefill_vector_rows(p.group, dtype);
     p.units_per_seq = (max_q_len + rows_per_wave - 1) / rows_per_wave;
     p.scale_log2 = scale * 1.4426950408889634f;
-    // the grid: (sequence, KV head) groups rounded up to whole rounds of XCDs
+    // the grid: (sequence, KV head) groups, rounded up to whole rounds of
+    // XCDs on the matrix-core path, times the row blocks of a chunk
     const int64_t groups = (int64_t)num_seqs * num_kv_heads;
-    if ((groups + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd * p.units_per_seq > 0x7fffffff)
-        return PA_ERR_SHAPE;
-    const hipError_t e = pa::launch_prefill(p, (hipStream_t)stream);
+    const int64_t padded = mfma ? (groups + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd : groups;
+    if (padded * p.units_per_seq > 0x7fffffff) return PA_ERR_SHAPE;
+    const hipError_t e = mfma ? pa::launch_prefill(p, (hipStream_t)stream)
+                              : pa::launch_prefill_vector(p, head_dim, dtype, (hipStream_t)stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -166,6 +166,11 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
 #endif
 constexpr int kPrefillGroups = PA_PREFILL_GROUPS;
 constexpr int kPrefillColumns = 16 * kPrefillGroups;
+// Prefill on the vector ALUs (every dtype / head_dim / block size): chunk rows
+// per wavefront for a group size, and the launch.
+int prefill_vector_rows(int group, int dtype);
+hipError_t launch_prefill_vector(const PrefillParams &p, int head_dim, int dtype,
+                                 hipStream_t stream);
 hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int num_pairs,
                               int num_blocks, int64_t block_bytes, hipStream_t stream);
 hipError_t launch_cache_write(const void *k, const void *v, void *k_cache, void *v_cache,

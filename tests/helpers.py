@@ -2,9 +2,20 @@
 
 Nothing here computes attention; the oracle and the GPU library do that.
 """
+import json
+import os
+
 import numpy as np
 
 from paged_kv_cache_261_amd import synthetic as S
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    """A fixture under tests/golden/ (each carries its citation)."""
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
 
 NAN_BITS = {"f32": np.uint32(0x7FC00000), "bf16": np.uint16(0x7FC0)}
 

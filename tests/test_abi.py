@@ -222,7 +222,8 @@ def prefill_call(lib, **kw):
 
 @needs_no_gpu
 @pytest.mark.parametrize("kw,status", [
-    (dict(d=64), UNSUP), (dict(dtype=0), UNSUP), (dict(bs=8, MB=16), UNSUP),
+    (dict(d=48), UNSUP), (dict(dtype=2), UNSUP), (dict(bs=12, MB=16), UNSUP),
+    (dict(bs=512, MB=1), UNSUP),
     (dict(Hq=34, Hkv=2), UNSUP), (dict(Hq=6, Hkv=4), SHAPE), (dict(B=-1), SHAPE),
     (dict(max_ctx=8 * 16 + 1), SHAPE), (dict(max_q=101), SHAPE),
     (dict(q=Z), NULL), (dict(cu=Z), NULL), (dict(out=MIS), ALIGN),

@@ -1084,3 +1084,129 @@ def test_prefill_workload_full_size():
         ref = pao.prefill_concat(w.q[q0:q1], kh, vh, w.tables[b:b + 1],
                                  np.array([0, q1 - q0]), w.ctx[b:b + 1], c.scale)
         H.assert_close_to_oracle(got[q0:q1], ref, "bf16", f"prefill workload seq {b}")
+
+
+# --------------------------------------------------------------------------
+# paged prefill on the vector ALUs (float32, other head dims and block sizes)
+# --------------------------------------------------------------------------
+def prefill_case_any(rng, chunks, prefixes, hq, hkv, d, bs, dtype):
+    ctxs = [p + c for p, c in zip(prefixes, chunks)]
+    q = S._normal(rng, (sum(chunks), hq, d), dtype)
+    kl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    vl = [S._normal(rng, (n, hkv, d), dtype) for n in ctxs]
+    nb = sum((n + bs - 1) // bs for n in ctxs) + 5
+    kc, vc, tab = H.paginate(kl, vl, bs, nb, rng, dtype)
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    return q, cu, np.array(ctxs, dtype=np.int32), kc, vc, tab
+
+
+@pytest.mark.parametrize("dtype,d,bs,G", [
+    ("f32", 16, 4, 1), ("f32", 64, 16, 1), ("f32", 32, 1, 3), ("f32", 128, 8, 4),
+    ("f32", 256, 16, 8), ("f32", 64, 64, 16), ("f32", 16, 256, 2),
+    ("bf16", 64, 16, 4), ("bf16", 32, 4, 8), ("bf16", 16, 16, 1), ("bf16", 256, 32, 3),
+    ("bf16", 128, 8, 4), ("bf16", 128, 4, 16), ("bf16", 64, 2, 5)])
+def test_prefill_vector_matches_oracle(dtype, d, bs, G):
+    """Shapes the matrix-core prefill does not take: chunks of 0, 1, a few and
+    many rows over empty, short and long prefixes, lengths off every block
+    and row-block boundary, unused slots NaN."""
+    rng = np.random.default_rng(7 * d + bs + G)
+    chunks = [1, 0, 7, 40, 33, 100, 5]
+    prefixes = [0, 12, 0, 1, 250, 77, 600]
+    hkv = 2
+    scale = 1 / math.sqrt(d)
+    q, cu, ctx, kc, vc, tab = prefill_case_any(rng, chunks, prefixes, hkv * G, hkv, d, bs, dtype)
+    ref = pao.prefill_concat(q, kc, vc, tab, cu, ctx, scale)
+    got = gpu_prefill(q, H.to_dev(kc), H.to_dev(vc), tab, cu, ctx, scale)
+    H.assert_close_to_oracle(got, ref, dtype, f"vector prefill {dtype} d {d} bs {bs} G {G}")
+
+
+def test_prefill_vector_out_of_range_block_is_left_out():
+    rng = np.random.default_rng(125)
+    q, cu, ctx, kc, vc, tab = prefill_case_any(rng, [40, 17, 1, 64], [100, 64, 32, 500], 4, 4,
+                                               64, 16, "f32")
+    nb = kc.shape[0]
+    bad = tab.copy()
+    bad[:, 1] = [nb, nb + 3, 1 << 29, -1]
+    tab_ref, ctx_ref = _drop_block(tab, ctx, 1, 16)
+    ref = pao.prefill_concat(q, kc, vc, tab_ref, cu, ctx_ref, 0.125)
+    got = gpu_prefill(q, H.to_dev(kc), H.to_dev(vc), bad, cu, ctx, 0.125)
+    H.assert_close_to_oracle(got, ref, "f32", "vector prefill with an out-of-range block")
+
+
+def test_prefill_demo1_prompt_then_decode():
+    """Lecture 7 demo 1 on the tiny workload's shape (4 heads, head_dim 16,
+    float32, block size 4): a pool of 8 blocks made non-contiguous by 5
+    allocations of which 3 are freed, a 7-token prompt prefilled (2 blocks,
+    the last 3/4 full), then two decode steps (the first fills the last slot,
+    the second takes a third block).  Every step's slot write goes through
+    pa_reshape_and_cache with the oracle pool's slots; the prefill and both
+    decodes match the oracle."""
+    g = H.golden("p2_demo1_block_table.json")["stated_on_page"]
+    hq = hkv = 4
+    d, bs = 16, g["block_size"]
+    rng = np.random.default_rng(71)
+    pool = Pool(g["pool_blocks"], bs)
+    junk = [pool.alloc() for _ in range(g["junk_allocs"])]
+    for i in g["junk_freed_indices"]:
+        pool.decref(junk[i])
+    cfg = S.Config(name="demo1", seed=0, num_seqs=1, num_q_heads=hq, num_kv_heads=hkv,
+                   head_dim=d, block_size=bs, num_blocks=g["pool_blocks"], max_blocks_per_seq=4,
+                   dtype="f32", scale=0.25, description="")
+    kh, vh = H.empty_pool(cfg)
+    kd, vd = H.dev_empty_pool(cfg)
+    seq = pool.seq_new()
+    k7 = S._normal(rng, (7, hkv, d), "f32")
+    v7 = S._normal(rng, (7, hkv, d), "f32")
+    slots = np.array([pool.append(seq)[0] for _ in range(7)])
+    pao.slot_write(kh, vh, k7, v7, slots, bs)
+    H.dev_write(kd, vd, k7, v7, slots)
+    tab = pool.table(seq, cfg.max_blocks_per_seq)[None]
+    assert (tab[0] >= 0).sum() == g["rows"][0]["n_blocks"]
+    q7 = S._normal(rng, (7, hq, d), "f32")
+    cu = np.array([0, 7], dtype=np.int32)
+    ref = pao.prefill_concat(q7, kh, vh, tab, cu, np.array([7]), 0.25)
+    got = gpu_prefill(q7, kd, vd, tab, cu, np.array([7]), 0.25)
+    H.assert_close_to_oracle(got, ref, "f32", "demo 1 prefill", report=True)
+    for step, row in enumerate(g["rows"][1:]):
+        kn = S._normal(rng, (1, hkv, d), "f32")
+        vn = S._normal(rng, (1, hkv, d), "f32")
+        slot = np.array([pool.append(seq)[0]])
+        pao.slot_write(kh, vh, kn, vn, slot, bs)
+        H.dev_write(kd, vd, kn, vn, slot)
+        tab = pool.table(seq, cfg.max_blocks_per_seq)[None]
+        n = pool.seq_len(seq)
+        assert n == row["tokens"] and (tab[0] >= 0).sum() == row["n_blocks"]
+        qn = S._normal(rng, (1, hq, d), "f32")
+        ref = pao.decode_concat(qn, kh, vh, tab, np.array([n]), 0.25)
+        for part in (0, -1, 4):
+            got = H.gpu_decode(qn, kd, vd, tab, np.array([n]), 0.25, None, part, VECTOR)
+            H.assert_close_to_oracle(got, ref, "f32", f"demo 1 decode {step + 1} part {part}")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "mha_f32"])
+def test_prefill_on_small_workload_shapes(name):
+    """The tiny and MHA float32 workloads' pools, prefilled instead of
+    decoded: every position of the tiny workload's four sequences (whole
+    prompts), and the last 1..96 positions of each MHA sequence (chunks over
+    cached prefixes, the shared prefix blocks included)."""
+    w = S.make_workload(name)
+    kd, vd = H.dev_pool(w)
+    kh, vh = H.oracle_pool(w)
+    ctx, tab = w.ctx_at(0), w.tables_at(0)
+    rng = np.random.default_rng(3)
+    if name == "tiny_f32":
+        chunks = ctx.copy()
+    else:
+        chunks = np.minimum(ctx, rng.integers(1, 97, size=len(ctx))).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = S._normal(rng, (int(cu[-1]), w.cfg.num_q_heads, w.cfg.head_dim), "f32")
+    ref = pao.prefill_concat(q, kh, vh, tab, cu, ctx, w.cfg.scale)
+    got = gpu_prefill(q, kd, vd, tab, cu, ctx, w.cfg.scale)
+    H.assert_close_to_oracle(got, ref, "f32", f"{name} prefill", report=True)
+    # one-row chunks are decodes: the same rows as the oracle's decode
+    one = np.ones(len(ctx), dtype=np.int32)
+    cu1 = np.concatenate([[0], np.cumsum(one)]).astype(np.int32)
+    q1 = w.q[0]
+    got1 = gpu_prefill(q1, kd, vd, tab, cu1, ctx, w.cfg.scale)
+    H.assert_close_to_oracle(got1, pao.decode_concat(q1, kh, vh, tab, ctx, w.cfg.scale), "f32",
+                             f"{name} one-row prefill")
