@@ -431,6 +431,69 @@ class DecodeRun:
         return {"wall_ms": wall * 1e3, "write": t_write, "main": t_main, "reduce": t_reduce,
                 "step": t_step, "cold": cold}
 
+    def tile_list(self):
+        """The 16-token (block, KV head) tiles the decode reads, in the order
+        of its tile stream (KV head slowest, then sequence or pack, then
+        tile); in shared-prefix mode a tile several members of a pack
+        reference is listed once.  Index = the tile's position in the pool
+        counted in 16-row tiles.  None where the block size is below 16."""
+        c, w = self.c, self.w
+        if c.block_size < 16:
+            return None
+        ctx, tab = w.ctx_at(0), w.tables_at(0)
+        per_block = c.block_size // 16
+        ids = []
+        if self.part == -3:
+            pack = 8
+            while pack > 1 and pack * (c.num_q_heads // c.num_kv_heads) > 32:
+                pack //= 2
+            for g in range(c.num_kv_heads):
+                for k0 in range(0, c.num_seqs, pack):
+                    mem = range(k0, min(c.num_seqs, k0 + pack))
+                    nt = max((int(ctx[b]) + 15) // 16 for b in mem)
+                    for t in range(nt):
+                        seen = []
+                        for b in mem:
+                            if t * 16 < int(ctx[b]):
+                                blk = int(tab[b, t * 16 // c.block_size])
+                                if blk not in seen:
+                                    seen.append(blk)
+                        ids += [(blk * c.num_kv_heads + g) * per_block + t % per_block
+                                for blk in seen]
+        else:
+            for g in range(c.num_kv_heads):
+                for b in range(c.num_seqs):
+                    t = np.arange((int(ctx[b]) + 15) // 16)
+                    blk = tab[b, t * 16 // c.block_size].astype(np.int64)
+                    ids.append((blk * c.num_kv_heads + g) * per_block + t % per_block)
+            ids = np.concatenate(ids) if ids else np.zeros(0, dtype=np.int64)
+        return np.asarray(ids, dtype=np.int32)
+
+    def paged_read(self, reps=20):
+        """The decode's own tiles read with no arithmetic (calibration kernel
+        pa_measure_tile_read): the paged-read ceiling of this workload."""
+        torch, pa = self.torch, self.pa
+        ids = self.tile_list()
+        if ids is None or len(ids) == 0:
+            return None
+        tiles = self.dev_t(ids)
+        sink = torch.empty(pa.MEASURE_SINK_WORDS, dtype=torch.int32, device=self.q.device)
+        stream = torch.cuda.current_stream()
+        for _ in range(3):
+            pa.pa_measure_tile_read(self.k_cache, self.v_cache, tiles, sink, stream=stream)
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pa.pa_measure_tile_read(self.k_cache, self.v_cache, tiles, sink, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        t = statistics.median(ms)
+        nbytes = int(len(ids)) * 2 * 16 * self.c.head_dim * (2 if self.c.dtype == "bf16" else 4)
+        return {"tiles": int(len(ids)), "bytes": nbytes, "ms": round(t, 5),
+                "GBs": round(nbytes / (t * 1e-3) / 1e9, 1), "kernel": "tile_read_kernel"}
+
     def bytes(self):
         c, w, ctx_h = self.c, self.w, self.ctx_h
         es = 2 if c.dtype == "bf16" else 4
@@ -450,7 +513,7 @@ class DecodeRun:
 
 def decode_record(run, t, steps, args):
     """The numbers of one timed decode workload (shared by the headline and
-    the extra workloads)."""
+    the extra workloads), with the paged-read ceiling of its own tiles."""
     c = run.c
     by = run.bytes()
     ms_step = t["wall_ms"] / steps
@@ -468,6 +531,13 @@ def decode_record(run, t, steps, args):
             "time": "plan + decode kernels (merge in frac_with_merge)" if shared
                     else "decode kernel (merge in frac_with_merge)"}
     traffic = load_traffic(c.name, run.algo_name, run.part)
+    pr = run.paged_read()
+    if pr is not None:
+        # the same tiles read with no arithmetic: how close the decode phase
+        # comes to a pure paged read of what it reads
+        pr["read_over_decode_kernel"] = round(pr["ms"] / main_ms, 4)
+        pr["read_over_decode_phase"] = round(pr["ms"] / (main_ms + red_ms), 4)
+        roof["paged_read"] = pr
     roof["traffic"] = traffic
     roof["traffic_source"] = ("rocprofv3 FETCH_SIZE/WRITE_SIZE per launch, committed in "
                               "profiles/traffic.json and taken on kernel sources that hash the "

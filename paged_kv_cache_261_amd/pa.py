@@ -47,6 +47,7 @@ def _load():
         "pa_decode_reduce": (I, [P, P, I, I, I, I, I, I, P, SZ, I, P]),
         "pa_decode_noalloc": (I, [P] * 6 + [I] * 8 + [F, I, I, I, P]),
         "pa_measure_stream_read": (I, [P, SZ, I, P, P]),
+        "pa_measure_tile_read": (I, [P, P, P, I, I, P, P]),
         "pa_status_string": (C.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
@@ -240,3 +241,18 @@ def pa_measure_stream_read(buf, sink, nontemporal=True, stream=None):
     _check(lib.pa_measure_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
                                       1 if nontemporal else 0, _dev(sink, "sink"),
                                       _stream(buf, stream)), "pa_measure_stream_read")
+
+
+def pa_measure_tile_read(k_cache, v_cache, tiles, sink, stream=None):
+    """Calibration only: read the (block, KV head) tiles listed in `tiles`
+    (int32, index block * num_kv_heads + head) of both caches the way the
+    decode kernels read them, with no arithmetic (the paged-read ceiling)."""
+    nb, hkv, bs, d = k_cache.shape
+    if tiles.dtype != torch.int32 or tiles.dim() != 1:
+        raise ValueError("tiles must be int32 [num_tiles]")
+    if sink.dtype != torch.int32 or sink.numel() < MEASURE_SINK_WORDS:
+        raise ValueError("sink must be an int32 tensor of MEASURE_SINK_WORDS words")
+    _check(lib.pa_measure_tile_read(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                    _dev(tiles, "tiles"), tiles.numel(),
+                                    bs * d * k_cache.element_size(), _dev(sink, "sink"),
+                                    _stream(k_cache, stream)), "pa_measure_tile_read")

@@ -38,7 +38,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) >= {"pa_reshape_and_cache", "pa_decode", "pa_decode_partitions",
                           "pa_decode_reduce", "pa_decode_workspace_size",
                           "pa_decode_auto_partition", "pa_status_string", "pa_copy_blocks",
-                          "pa_prefill", "pa_decode_noalloc", "pa_measure_stream_read"}
+                          "pa_prefill", "pa_decode_noalloc", "pa_measure_stream_read",
+                          "pa_measure_tile_read"}
     raw = C.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), n
@@ -158,6 +159,10 @@ def test_stream_read_rejects_bad_arguments(lib):
     assert lib.pa_measure_stream_read(A, 1 << 20, 1, Z, Z) == NULL
     assert lib.pa_measure_stream_read(MIS, 1 << 20, 1, A, Z) == ALIGN
     assert lib.pa_measure_stream_read(A, (1 << 20) + 8, 0, A, Z) == ALIGN
+    assert lib.pa_measure_tile_read(A, A, Z, 10, 4096, A, Z) == NULL
+    assert lib.pa_measure_tile_read(A, A, A, 0, 4096, A, Z) == SHAPE
+    assert lib.pa_measure_tile_read(A, A, A, 10, 3000, A, Z) == UNSUP
+    assert lib.pa_measure_tile_read(MIS, A, A, 10, 4096, A, Z) == ALIGN
 
 
 @needs_no_gpu

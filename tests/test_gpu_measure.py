@@ -26,3 +26,25 @@ def test_stream_read_reads_every_byte(nbytes, nt):
     got = np.bitwise_xor.reduce(sink.cpu().numpy())
     want = np.bitwise_xor.reduce(host)
     assert got == want
+
+
+@pytest.mark.parametrize("tile_bytes,n_tiles", [(4096, 1), (4096, 5000), (1024, 777),
+                                                (2048, 3000), (8192, 1025)])
+def test_tile_read_reads_every_listed_tile(tile_bytes, n_tiles):
+    """The paged tile-read calibration reads exactly the listed tiles of both
+    pools (repeats included): its XOR equals the XOR over those tiles."""
+    rng = np.random.default_rng(tile_bytes + n_tiles)
+    words = tile_bytes // 4
+    pool_tiles = 4096
+    k = rng.integers(-2**31, 2**31, size=(pool_tiles, words), dtype=np.int64).astype(np.int32)
+    v = rng.integers(-2**31, 2**31, size=(pool_tiles, words), dtype=np.int64).astype(np.int32)
+    ids = rng.integers(0, pool_tiles, size=n_tiles).astype(np.int32)
+    # as caches [NB, Hkv, bs, d] of float32 with one tile = bs * d * 4 bytes
+    kd = torch.from_numpy(k.view(np.float32)).cuda().view(pool_tiles, 1, 16, words // 16)
+    vd = torch.from_numpy(v.view(np.float32)).cuda().view(pool_tiles, 1, 16, words // 16)
+    sink = torch.full((pa.MEASURE_SINK_WORDS,), -1, dtype=torch.int32, device="cuda")
+    pa.pa_measure_tile_read(kd, vd, torch.from_numpy(ids).cuda(), sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy())
+    want = np.bitwise_xor.reduce(np.concatenate([k[ids].ravel(), v[ids].ravel()]))
+    assert got == want
