@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU work for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="time only --config (no shared-prefix / long-context records, no "
+                         "streaming-read ceiling): for per-workload profiler runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the benchmark, copy a 1 GiB buffer with torch 5 times "
                          "(reference for scaling HBM byte counters)")
@@ -680,7 +683,7 @@ def main():
     result["copy_blocks"] = copy_rec
 
     default_run = args.config == DEFAULT_CONFIG and args.partition is None and \
-        args.algo == "auto"
+        args.algo == "auto" and not args.no_extra_workloads
     if default_run:
         result["workloads"] = {}
         for name in EXTRA_WORKLOADS:

@@ -1210,3 +1210,15 @@ def test_prefill_on_small_workload_shapes(name):
     got1 = gpu_prefill(q1, kd, vd, tab, cu1, ctx, w.cfg.scale)
     H.assert_close_to_oracle(got1, pao.decode_concat(q1, kh, vh, tab, ctx, w.cfg.scale), "f32",
                              f"{name} one-row prefill")
+
+
+def test_prefill_negative_scale_matches_oracle():
+    """A negative or zero scale (every key weighs the same at 0) matches the
+    oracle on the matrix-core shape."""
+    rng = np.random.default_rng(9)
+    q, cu, ctx, kc, vc, tab = prefill_case_any(rng, [5, 40, 1], [30, 0, 200], 8, 2, 128, 16,
+                                               "bf16")
+    for scale in (-0.09, 0.0):
+        ref = pao.prefill_concat(q, kc, vc, tab, cu, ctx, scale)
+        got = gpu_prefill(q, H.to_dev(kc), H.to_dev(vc), tab, cu, ctx, scale)
+        H.assert_close_to_oracle(got, ref, "bf16", f"prefill with scale {scale}")
