@@ -13,8 +13,9 @@
 //            across the 4 lane groups with two row-swap permutes, and the
 //            reference max lags the running max by at most 8 (lazy rescale);
 //   P.V      O^T[128 x 16] += V_tile^T[128 x 16 tokens] . P^T[16 x 16]
-//            8 x v_mfma_f32_16x16x16_bf16 (P rounded to bfloat16, fp32
-//            accumulation).
+//            2 x 8 x v_mfma_f32_16x16x16_bf16: P as the sum of two bfloat16
+//            parts (its high part and what rounding dropped), fp32
+//            accumulation.
 //
 // Register layouts (lane = 16 * grp + row16; column = row16):
 //  - S: lane holds S[token 4*grp + i][column row16], i = 0..3 -- exactly the
@@ -180,11 +181,21 @@ __device__ __forceinline__ void tile_update_v(const u32x4 (&kr)[4], VOp &&v_op,
 #pragma unroll
         for (int nn = 0; nn < 8; nn++) a.o[nn] *= alpha;
     }
-    const s16x4 pb = __builtin_bit_cast(
-        s16x4, (uint2){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
+    // P enters the product as two bfloat16 parts, hi = bf16(p) and
+    // lo = bf16(p - hi), so its rounding costs 2^-17 of a weight instead of
+    // 2^-9; the second product is free here, where the tile loads set the
+    // pace
+    const uint32_t h01 = pack_bf16x2(pr[0], pr[1]), h23 = pack_bf16x2(pr[2], pr[3]);
+    const s16x4 pb = __builtin_bit_cast(s16x4, (uint2){h01, h23});
+    const s16x4 pl = __builtin_bit_cast(
+        s16x4, (uint2){pack_bf16x2(pr[0] - bf16_lo(h01), pr[1] - bf16_hi(h01)),
+                       pack_bf16x2(pr[2] - bf16_lo(h23), pr[3] - bf16_hi(h23))});
 #pragma unroll
-    for (int nn = 0; nn < 8; nn++)
-        a.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_op(nn), pb, a.o[nn], 0, 0, 0);
+    for (int nn = 0; nn < 8; nn++) {
+        const s16x4 vo = v_op(nn);
+        a.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vo, pb, a.o[nn], 0, 0, 0);
+        a.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vo, pl, a.o[nn], 0, 0, 0);
+    }
 }
 
 // The tile step on V as loaded by load_tile_rows: product nn takes dim
