@@ -159,8 +159,8 @@ int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int
  *
  * Supported: head_dim in {16, 32, 64, 128, 256}; block_size a power of two in
  * [1, 256]; group size at most 16; dtype PA_F32 or PA_BF16.  bfloat16 with
- * head_dim 128 and block_size >= 16 runs on the matrix cores, every other
- * shape on the vector ALUs (float32 arithmetic either way).  Chunks with
+ * head_dim 128, block_size >= 16 and scale > 0 runs on the matrix cores,
+ * everything else on the vector ALUs (float32 arithmetic either way).  Chunks with
  * n_b = 0 produce nothing.  Asynchronous on `stream`, no workspace.
  */
 int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,

@@ -402,8 +402,10 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
     if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || !block_size_ok(block_size) ||
         num_q_heads / num_kv_heads > 16)
         return PA_ERR_UNSUPPORTED;
-    // the matrix-core kernel where its tile applies, the vector ALUs elsewhere
-    const bool mfma = balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads);
+    // the matrix-core kernel where its tile applies (it folds a positive
+    // scale into the exponent), the vector ALUs elsewhere
+    const bool mfma = balanced_applies(dtype, head_dim, block_size, num_q_heads, num_kv_heads) &&
+                      scale > 0.f;
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size ||
         max_q_len > max_context_len)
         return PA_ERR_SHAPE;

@@ -160,12 +160,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // Launchers: validate nothing (pa_api.cpp does), enqueue, return hipError_t.
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
-// query-head columns one prefill wavefront serves (16-column groups)
-#ifndef PA_PREFILL_GROUPS
-#define PA_PREFILL_GROUPS 1
-#endif
-constexpr int kPrefillGroups = PA_PREFILL_GROUPS;
-constexpr int kPrefillColumns = 16 * kPrefillGroups;
+// query-head columns one matrix-core prefill wavefront serves (the 32
+// columns of the 32x32x16 product)
+constexpr int kPrefillColumns = 32;
 // Prefill on the vector ALUs (every dtype / head_dim / block size): chunk rows
 // per wavefront for a group size, and the launch.
 int prefill_vector_rows(int group, int dtype);

@@ -10,15 +10,16 @@
 // p = context_lens[b] - n_b + r attends over positions 0..p.
 //
 // How (matrix cores; bf16, head_dim 128, block_size >= 16, group size
-// G <= 16): one wavefront serves 16 query-head columns of one KV head (16 x
-// kPrefillGroups with the compile-time knob) -- the G heads of TPU = 16 / G
-// consecutive chunk rows -- and walks the keys 0 .. (the last row's
-// position) two 16-token tiles at a time: both score products (the decode
-// tile step's layouts), one online-softmax update over the 32 keys, and P.V
-// on the 16x16x32 matrix-core product; a column's causal limit is its row's
-// position, so the last tiles are partly masked per column.  A workgroup of
-// kWgWaves such wavefronts (consecutive units of one (sequence, KV head))
-// reads each K/V tile from memory once and shares it through LDS.
+// G <= 16, scale > 0): one wavefront serves 32 query-head columns of one KV
+// head -- the G heads of 32 / G consecutive chunk rows -- on the
+// 32x32x16 bf16 product, and walks the keys 0 .. (the last row's position)
+// two 16-token tiles at a time: 8 score products S[32 keys x 32 columns],
+// one online-softmax update over the 32 keys, and 8 P.V products; a
+// column's causal limit is its row's position, applied only on the steps
+// that reach past some column's row (or hold a tile with an invalid block
+// id).  A workgroup of kWgWaves such wavefronts (consecutive units of one
+// (sequence, KV head)) reads each K/V tile from memory once and shares it
+// through LDS.
 //
 // Order of the workgroups: a unit's work grows with its sequence's context
 // and its rows' positions, and the grid is many times larger than what is
@@ -53,23 +54,24 @@ __device__ __forceinline__ int seq_of_rank(const PrefillParams &p, const int32_t
 constexpr int kPrefillCols = kPrefillColumns;
 
 #ifndef PA_PREFILL_WAVES_PER_EU
-#define PA_PREFILL_WAVES_PER_EU 4
+#define PA_PREFILL_WAVES_PER_EU 3
 #endif
 
 // ---------------------------------------------------------------------------
 // Each tile (16 rows of K and of V, 8 KiB) is read from memory once per
 // workgroup in 16-byte pieces, so every request covers whole 128-byte
-// lines; the wavefronts then read their operands out of LDS: K in the
-// register layout of the decode tile step, V through the transposing LDS
-// read.  LDS rows are padded (below), so the 16 lanes that read one column
-// of 16 K rows do not all fall in the same banks.  Four stages form a ring:
+// lines; the wavefronts then read their operands out of LDS: K as the
+// score product's first operand (lane l: key l % 32 of the pair, 8 dims
+// from 8 (l / 32) per 16-dim step), V through the transposing LDS read.
+// LDS rows are padded (below), so the lanes that read one dim range of
+// 32 K rows do not all fall in the same banks.  Four stages form a ring:
 // while tiles 2p and 2p+1 are read and computed out of two of them, tiles
 // 2p+2 and 2p+3 (loaded during the step before) are written into the other
 // two and tiles 2p+4 and 2p+5 are loaded; one LDS-only barrier per step (no
 // wait on the loads in flight).
 // ---------------------------------------------------------------------------
 #ifndef PA_PREFILL_WG_WAVES
-#define PA_PREFILL_WG_WAVES 8
+#define PA_PREFILL_WG_WAVES 4
 #endif
 constexpr int kWgWaves = PA_PREFILL_WG_WAVES;
 constexpr int kWgThreads = kWave * kWgWaves;
@@ -77,14 +79,19 @@ constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kPieces = 2 * kTile * kRowBytes / 16;
 static_assert(kPieces % kWgThreads == 0, "tile pieces must divide over the workgroup");
 constexpr int kPiecesPerThread = kPieces / kWgThreads;
-// LDS row padding in bytes, measured: 32 for K and V (288-byte rows) is
-// best; 16 or 64 run 6% slower, and unpadded V rows nearly halve the speed
-// (the transposing reads of four rows then fall in the same banks)
+// LDS row padding in bytes.  K rows of 272 bytes (68 banks of 4 bytes):
+// the 16 rows that one K read spans start 4 banks apart and cover all 64.
+// V rows of 320 bytes (80 banks): the four rows of one transposing read
+// start 16 banks apart, and with the two 32-byte column halves the 32
+// lanes of a pass cover all 64 banks.  Measured: no bank conflicts, where
+// 288-byte rows for both had 17 M conflict cycles per launch of the
+// chunked-prefill workload and ran 1.5% slower; unpadded V rows nearly
+// halve the speed.
 #ifndef PA_PREFILL_KPAD
-#define PA_PREFILL_KPAD 32
+#define PA_PREFILL_KPAD 16
 #endif
 #ifndef PA_PREFILL_VPAD
-#define PA_PREFILL_VPAD 32
+#define PA_PREFILL_VPAD 64
 #endif
 constexpr int kLdsRowK = kRowBytes + PA_PREFILL_KPAD;   // LDS row strides (padded)
 constexpr int kLdsRowV = kRowBytes + PA_PREFILL_VPAD;
@@ -97,66 +104,61 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Two consecutive tiles A and B in one step: both score products, one
-// softmax update over their 32 keys, and P.V as one
-// v_mfma_f32_16x16x32_bf16 per product whose k slots 8 grp .. 8 grp + 3
-// hold tile A's tokens 4 grp .. 4 grp + 3 and 8 grp + 4 .. 8 grp + 7 tile
-// B's -- the order in which the lane holds P.  okA / okB: the tile's block
-// id is valid (a tile with an invalid id contributes nothing).
-// The operands come straight out of the two stages, K of A, then K of B,
-// then V, with scheduling fences between the score products, so no more
-// than one tile's K is in registers at a time (the step fits four
-// wavefronts per SIMD).
-__device__ __forceinline__ void read_k(const char *stage, Lane ln, u32x4 (&kr)[4]) {
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Softmax state of one wavefront for its 32 columns (32x32x16 products):
+// O^T block mb (dims 32 mb .. 32 mb + 31): lane holds column lane % 32 at
+// dims 32 mb + 8 i + 4 (lane / 32) + j in o[mb][4 i + j].
+struct Acc32 {
+    f32x16 o[4];
+    float m;
+    float lsum;      // this lane's share (the other 16 keys sit in lane ^ 32)
+};
+
+// One step over a pair of 16-key tiles (32 keys) for the 32 columns.
+//  scores: S[32 keys x 32 columns] = K_pair . Q^T, 8 x v_mfma_f32_32x32x16_bf16;
+//          the lane holds column lane % 32 at keys 8 i + 4 (lane / 32) + j;
+//  softmax: per column over its 16 keys and the partner lane's 16;
+//  P.V:    O^T[32 mb + .., col] += V^T[dims, 16 keys] . P[16 keys, cols],
+//          2 key blocks x 4 dim blocks; key block kb's k slot 8 h + 4 i' + j
+//          is key 16 kb + 8 i' + 4 h + j (h = lane / 32) -- the order in
+//          which the lane holds P -- and V arrives through the transposing
+//          LDS read in the same order.
+__device__ __forceinline__ void pair_update32(const char *stA, const char *stB,
+                                              const bf16x8 (&qv)[8], int nv, bool okA, bool okB,
+                                              float scale_log2, Acc32 &a, int lane) {
+    const int col = lane & 31, half = lane >> 5;
+    const char *krow = (col < 16 ? stA : stB) + (col & 15) * kLdsRowK + half * 16;
+    f32x16 S = {};
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-        kr[j] = *(const u32x4 *)(stage + ln.row16 * kLdsRowK + ln.grp * 16 + 64 * j);
-}
-__device__ __forceinline__ s16x4 read_vt(const char *stage, Lane ln, int nn) {
-    const char *vrow =
-        stage + kVBase + (4 * ln.grp + (ln.row16 >> 2)) * kLdsRowV + (ln.row16 & 3) * 8;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(vrow + 32 * nn));
-}
-// scheduling fences in the pair step: bit 0 after tile A's scores, bit 1
-// after tile B's, bit 2 before the V reads (measured: 3 best, 0.2% over 7)
-#ifndef PA_PAIR_FENCES
-#define PA_PAIR_FENCES 3
-#endif
-__device__ __forceinline__ void pair_update(const char *stA, const char *stB,
-                                            const bf16x8 (&qv)[4], int nv, bool okA, bool okB,
-                                            float scale_log2, Acc &a, Lane ln) {
-    f32x4 SA = {0.f, 0.f, 0.f, 0.f}, SB = {0.f, 0.f, 0.f, 0.f};
-    {
-        u32x4 kr[4];
-        read_k(stA, ln, kr);
-#pragma unroll
-        for (int kk = 0; kk < 4; kk++)
-            SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
-                                                         qv[kk], SA, 0, 0, 0);
+    for (int kk = 0; kk < 8; kk++) {
+        const u32x4 kr = *(const u32x4 *)(krow + 32 * kk);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr), qv[kk], S, 0,
+                                                    0, 0);
     }
-    if (PA_PAIR_FENCES & 1) __builtin_amdgcn_sched_barrier(0);
-    {
-        u32x4 kr[4];
-        read_k(stB, ln, kr);
+    float s[16];
+    // a valid column sees every key of the pair unless the pair reaches past
+    // its row or holds a tile with an invalid block id: then mask
+    const bool need_mask = __ballot(nv < 32) != 0 || !okA || !okB;
+    if (need_mask) {
+        const int limA = okA ? nv : 0;
+        const int limB = okB ? nv : 0;
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++)
-            SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
-                                                         qv[kk], SB, 0, 0, 0);
-    }
-    if (PA_PAIR_FENCES & 2) __builtin_amdgcn_sched_barrier(0);
-    // visible rows of each tile for this column (none when its block id is invalid)
-    const int limA = okA ? nv : 0;
-    const int limB = okB ? nv - kTile : 0;
-    float s[8];
+        for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        s[i] = 4 * ln.grp + i < limA ? SA[i] * scale_log2 : -INFINITY;
-        s[4 + i] = 4 * ln.grp + i < limB ? SB[i] * scale_log2 : -INFINITY;
+            for (int j = 0; j < 4; j++) {
+                const int key = 8 * i + 4 * half + j;
+                const int lim = i < 2 ? limA : limB;
+                s[4 * i + j] = key < lim ? S[4 * i + j] : -INFINITY;
+            }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; e++) s[e] = S[e];
     }
-    const float lmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                             fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    const float tmax = xor32_max(xor16_max(lmax));
+    float lmax = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; e++) lmax = fmaxf(lmax, s[e]);
+    const float tmax = xor32_max(lmax) * scale_log2;
 #if PA_RESCALE_SLACK > 0
     const float m_new = tmax > a.m + (float)PA_RESCALE_SLACK ? tmax : a.m;
 #else
@@ -164,26 +166,50 @@ __device__ __forceinline__ void pair_update(const char *stA, const char *stB,
 #endif
     const float shift = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(a.m - shift);
-    float pr[8];
+    float pr[16];
 #pragma unroll
-    for (int i = 0; i < 8; i++) pr[i] = fast_exp2(s[i] - shift);
-    a.lsum = a.lsum * alpha +
-             (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+    for (int e = 0; e < 16; e++) pr[e] = fast_exp2(fmaf(s[e], scale_log2, -shift));
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e++) ls += pr[e];
+    a.lsum = a.lsum * alpha + ls;
     a.m = m_new;
     if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
-        for (int nn = 0; nn < 8; nn++) a.o[nn] *= alpha;
+        for (int mb = 0; mb < 4; mb++) a.o[mb] *= alpha;
     }
-    const bf16x8 pb = __builtin_bit_cast(
-        bf16x8, (u32x4){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
-    if (PA_PAIR_FENCES & 4) __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pk[2];
 #pragma unroll
-    for (int nn = 0; nn < 8; nn++) {
-        const uint2 x = __builtin_bit_cast(uint2, read_vt(stA, ln, nn));
-        const uint2 y = __builtin_bit_cast(uint2, read_vt(stB, ln, nn));
-        a.o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, (u32x4){x.x, x.y, y.x, y.y}), pb, a.o[nn], 0, 0, 0);
+    for (int kb = 0; kb < 2; kb++)
+        pk[kb] = __builtin_bit_cast(
+            bf16x8, (u32x4){pack_bf16x2(pr[8 * kb + 0], pr[8 * kb + 1]),
+                            pack_bf16x2(pr[8 * kb + 2], pr[8 * kb + 3]),
+                            pack_bf16x2(pr[8 * kb + 4], pr[8 * kb + 5]),
+                            pack_bf16x2(pr[8 * kb + 6], pr[8 * kb + 7])});
+    // transposing V reads: lane q of each 16-lane group reads 4 dims of key
+    // row 8 i' + 4 half + q / 4 of the tile; lane i of the group receives
+    // one dim (dbase + i) of the 4 keys
+    const int q = lane & 15, g16 = lane >> 4;
+    const int vrow0 = 4 * half + (q >> 2);
+    const int vcol = (16 * (g16 & 1) + 4 * (q & 3)) * 2;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+        const char *vt = (kb == 0 ? stA : stB) + kVBase + vcol;
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+            const uint2 x = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (__attribute__((address_space(3))) s16x4 *)(vt + vrow0 * kLdsRowV +
+                                                                        64 * mb)));
+            const uint2 y = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (__attribute__((address_space(3))) s16x4 *)(vt + (vrow0 + 8) *
+                                                                                 kLdsRowV +
+                                                                        64 * mb)));
+            a.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, (u32x4){x.x, x.y, y.x, y.y}), pk[kb], a.o[mb], 0, 0,
+                0);
+        }
     }
 }
 constexpr int kStages = 4;
@@ -198,11 +224,9 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const Lane ln{lane & 15, lane >> 4};
     const int G = p.group;
     const int TPU = kPrefillCols / G;
     const int ubs = (p.units_per_seq + kWgWaves - 1) / kWgWaves;   // unit blocks per group
-    // workgroup -> (XCD, slot on it) -> group i = (rank, KV head), unit block
     const int xcd = blockIdx.x % kNumXcd;
     const int slot = blockIdx.x / kNumXcd;
     const int i = (slot / ubs) * kNumXcd + xcd;
@@ -222,29 +246,30 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
     const int r0 = wg_r0 + wave * TPU;                        // this wavefront's first row
     const int r_end = min(nq, r0 + TPU);                      // r_end <= r0: no rows
 
-    int ncol[kPrefillGroups], rowid[kPrefillGroups], head[kPrefillGroups];
-    bool ok[kPrefillGroups];
-    bf16x8 qv[kPrefillGroups][4];
-    Acc a[kPrefillGroups];
-#pragma unroll
-    for (int cg = 0; cg < kPrefillGroups; cg++) {
-        const int col = cg * 16 + ln.row16;
-        const int r = r0 + col / G;
-        head[cg] = g * G + col % G;
-        ok[cg] = col / G < TPU && r < r_end;
-        rowid[cg] = q0 + r;
-        ncol[cg] = ok[cg] ? first_pos + r + 1 : 0;
+    // column lane % 32 = (row r0 + col / G, head g G + col % G)
+    const int col = lane & 31, half = lane >> 5;
+    const int r = r0 + col / G;
+    const int head = g * G + col % G;
+    const bool ok = col / G < TPU && r < r_end;
+    const int rowid = q0 + r;
+    const int ncol = ok ? first_pos + r + 1 : (1 << 30);
+    bf16x8 qv[8];
+    {
         const char *qrow = (const char *)p.q +
-                           (((size_t)(ok[cg] ? rowid[cg] : q0) * p.num_q_heads +
-                             (ok[cg] ? head[cg] : 0)) * kD + 8 * ln.grp) * 2;
+                           (((size_t)(ok ? rowid : q0) * p.num_q_heads + (ok ? head : 0)) * kD) * 2 +
+                           16 * half;
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
-            u32x4 raw = *(const u32x4 *)(qrow + 64 * kk);
-            if (!ok[cg]) raw = (u32x4){0u, 0u, 0u, 0u};
-            qv[cg][kk] = __builtin_bit_cast(bf16x8, raw);
+        for (int kk = 0; kk < 8; kk++) {
+            u32x4 raw = *(const u32x4 *)(qrow + 32 * kk);
+            if (!ok) raw = (u32x4){0u, 0u, 0u, 0u};
+            qv[kk] = __builtin_bit_cast(bf16x8, raw);
         }
-        acc_init(a[cg]);
     }
+    Acc32 a;
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++) a.o[mb] = (f32x16){};
+    a.m = -INFINITY;
+    a.lsum = 0.f;
 
     const char *kbase = (const char *)p.k_cache;
     const char *vbase = (const char *)p.v_cache;
@@ -253,8 +278,6 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
     const int bs_mask = (1 << log2bs) - 1;
     const int ntiles = (kmax + kTile - 1) / kTile;
     auto phys_of = [&](int t) -> int { return table[(min(t, ntiles - 1) * kTile) >> log2bs]; };
-    // thread tid moves pieces tid, tid + kWgThreads, ...: piece c is bytes
-    // 16 (c % 16) .. of row (c / 16) % 16 of K (c < 256) or of V
     auto issue = [&](int t, int phys, u32x4 (&gr)[kPiecesPerThread]) {
         const bool in = t < ntiles && (unsigned)phys < (unsigned)p.num_blocks;
         const int rows = in ? min(kTile, kmax - t * kTile) : 0;
@@ -264,8 +287,6 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
         for (int j = 0; j < kPiecesPerThread; j++) {
             const int c = tid + j * kWgThreads;
             const int goff = ((c >> 4) & (kTile - 1)) * kRowBytes + (c & 15) * 16;
-            // K or V is the same for the whole wavefront (256 is a multiple of
-            // 64), so only that pool's descriptor is built
             const bool of_k = wave * kWave + j * kWgThreads < kPieces / 2;
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)((of_k ? kbase : vbase) + off), (short)0, rows * kRowBytes, kRsrcWord3);
@@ -278,27 +299,12 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
 #pragma unroll
         for (int j = 0; j < kPiecesPerThread; j++) {
             const int c = tid + j * kWgThreads;
-            const int row = c >> 4;   // 0..15: K row, 16..31: V row
+            const int row = c >> 4;
             const int lo = row < kTile ? row * kLdsRowK : kVBase + (row - kTile) * kLdsRowV;
             *(u32x4 *)(base + lo + (c & 15) * 16) = gr[j];
         }
     };
-    // O / l of column row16 in bfloat16: a.o[nn][i] holds dim 16 nn + 4 grp + i
-    auto store_out_row = [&](char *out_row, const Acc &acc) {
-        const float inv = acc.lsum > 0.f ? 1.f / acc.lsum : 0.f;
-        char *dst = out_row + 8 * ln.grp;
-#pragma unroll
-        for (int nn = 0; nn < 8; nn++)
-            *(uint2 *)(dst + 32 * nn) =
-                (uint2){pack_bf16x2(acc.o[nn][0] * inv, acc.o[nn][1] * inv),
-                        pack_bf16x2(acc.o[nn][2] * inv, acc.o[nn][3] * inv)};
-    };
 
-    // tiles 2p and 2p+1 are computed in step p out of stages (2p) % 4 and
-    // (2p+1) % 4; tiles 2p+2, 2p+3 (loaded during step p-1) are written into
-    // the stages step p-1 read, and tiles 2p+4, 2p+5 are loaded.  Tiles past
-    // the last are written too (as zeros: their loads read nothing), so no
-    // stale LDS bits meet a zero probability.
     const int ntiles2 = (ntiles + 1) & ~1;
     u32x4 gr[2][kPiecesPerThread];
     int phA = phys_of(0), phB = phys_of(1);
@@ -314,10 +320,8 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
         const int sa = t & 3;
         const bool okA = (unsigned)phA < (unsigned)p.num_blocks;
         const bool okB = (unsigned)phB < (unsigned)p.num_blocks;
-#pragma unroll
-        for (int cg = 0; cg < kPrefillGroups; cg++)
-            pair_update(lds + sa * kStage, lds + (sa + 1) * kStage, qv[cg], ncol[cg] - t * kTile,
-                        okA, okB, p.scale_log2, a[cg], ln);
+        pair_update32(lds + sa * kStage, lds + (sa + 1) * kStage, qv, ncol - t * kTile, okA, okB,
+                      p.scale_log2, a, lane);
         if (t + 2 < ntiles2) {
             stage_write((t + 2) & 3, gr[0]);
             stage_write((t + 3) & 3, gr[1]);
@@ -330,12 +334,17 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
         issue(t + 5, phD, gr[1]);
         lds_barrier();
     }
+    const float lsum = xor32_sum(a.lsum);
+    if (ok) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        char *orow = (char *)out + ((size_t)rowid * p.num_q_heads + head) * kD * 2;
 #pragma unroll
-    for (int cg = 0; cg < kPrefillGroups; cg++) {
-        acc_finish(a[cg]);
-        if (ok[cg])
-            store_out_row((char *)out + ((size_t)rowid[cg] * p.num_q_heads + head[cg]) * kD * 2,
-                          a[cg]);
+        for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+            for (int ii = 0; ii < 4; ii++)
+                *(uint2 *)(orow + (32 * mb + 8 * ii + 4 * half) * 2) =
+                    (uint2){pack_bf16x2(a.o[mb][4 * ii + 0] * inv, a.o[mb][4 * ii + 1] * inv),
+                            pack_bf16x2(a.o[mb][4 * ii + 2] * inv, a.o[mb][4 * ii + 3] * inv)};
     }
 }
 

@@ -1213,8 +1213,9 @@ def test_prefill_on_small_workload_shapes(name):
 
 
 def test_prefill_negative_scale_matches_oracle():
-    """A negative or zero scale (every key weighs the same at 0) matches the
-    oracle on the matrix-core shape."""
+    """A non-positive scale sends the bf16 head_dim-128 shape to the vector
+    ALUs (the matrix-core step folds a positive scale into the exponent);
+    the result still matches the oracle (at 0 every key weighs the same)."""
     rng = np.random.default_rng(9)
     q, cu, ctx, kc, vc, tab = prefill_case_any(rng, [5, 40, 1], [30, 0, 200], 8, 2, 128, 16,
                                                "bf16")
