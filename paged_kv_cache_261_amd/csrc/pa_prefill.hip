@@ -59,44 +59,40 @@ constexpr int kPrefillCols = kPrefillColumns;
 
 // ---------------------------------------------------------------------------
 // Each tile (16 rows of K and of V, 8 KiB) is read from memory once per
-// workgroup in 16-byte pieces, so every request covers whole 128-byte
-// lines; the wavefronts then read their operands out of LDS: K as the
-// score product's first operand (lane l: key l % 32 of the pair, 8 dims
-// from 8 (l / 32) per 16-dim step), V through the transposing LDS read.
-// LDS rows are padded (below), so the lanes that read one dim range of
-// 32 K rows do not all fall in the same banks.  Four stages form a ring:
-// while tiles 2p and 2p+1 are read and computed out of two of them, tiles
-// 2p+2 and 2p+3 (loaded during the step before) are written into the other
-// two and tiles 2p+4 and 2p+5 are loaded; one LDS-only barrier per step (no
-// wait on the loads in flight).
+// workgroup, straight into an LDS stage by buffer loads with an LDS
+// destination: one such load moves 1 KiB (64 lanes x 16 bytes, four rows),
+// and each of the four wavefronts moves two of a tile's eight (K rows 0-15
+// by wavefronts 0 and 1, V rows by 2 and 3).  The wavefronts then read their
+// operands out of LDS: K as the score product's first operand (lane l: key
+// l % 32 of the pair, 8 dims from 8 (l / 32) per 16-dim step), V through the
+// transposing LDS read.
+//
+// A load writes its 64 lanes' bytes contiguously, so rows cannot be padded;
+// instead the 16 16-byte pieces of a row are permuted (the permutation is
+// applied to the global addresses the lanes load from): K row r holds
+// piece c at slot c ^ r, so the 16 rows that one K read spans sit in 16
+// different slots and cover all 64 banks; V row r holds piece c at slot
+// c ^ 4 (r & 3), so the four rows of one transposing read start 16 banks
+// apart.  No bank conflicts either way.
+//
+// Six stages (three pairs) form a ring: step p computes pair p out of two
+// of them while pair p+1 (issued the step before) lands, and first issues
+// pair p+2 into the two that pair p-1 used; before its barrier each
+// wavefront waits for its own loads of pair p+1 (the four it issued most
+// recently, pair p+2's, stay in flight).  Loads past a descriptor's size
+// write zeros, so rows past the context and tiles past the last arrive as
+// zeros, and no stale LDS bits meet a zero probability.
 // ---------------------------------------------------------------------------
 #ifndef PA_PREFILL_WG_WAVES
 #define PA_PREFILL_WG_WAVES 4
 #endif
 constexpr int kWgWaves = PA_PREFILL_WG_WAVES;
+static_assert(kWgWaves == 4, "each wavefront moves two 1 KiB quarters of K or of V per tile");
 constexpr int kWgThreads = kWave * kWgWaves;
-// 16-byte pieces of one tile: 256 of K, then 256 of V
-constexpr int kPieces = 2 * kTile * kRowBytes / 16;
-static_assert(kPieces % kWgThreads == 0, "tile pieces must divide over the workgroup");
-constexpr int kPiecesPerThread = kPieces / kWgThreads;
-// LDS row padding in bytes.  K rows of 272 bytes (68 banks of 4 bytes):
-// the 16 rows that one K read spans start 4 banks apart and cover all 64.
-// V rows of 320 bytes (80 banks): the four rows of one transposing read
-// start 16 banks apart, and with the two 32-byte column halves the 32
-// lanes of a pass cover all 64 banks.  Measured: no bank conflicts, where
-// 288-byte rows for both had 17 M conflict cycles per launch of the
-// chunked-prefill workload and ran 1.5% slower; unpadded V rows nearly
-// halve the speed.
-#ifndef PA_PREFILL_KPAD
-#define PA_PREFILL_KPAD 16
-#endif
-#ifndef PA_PREFILL_VPAD
-#define PA_PREFILL_VPAD 64
-#endif
-constexpr int kLdsRowK = kRowBytes + PA_PREFILL_KPAD;   // LDS row strides (padded)
-constexpr int kLdsRowV = kRowBytes + PA_PREFILL_VPAD;
-constexpr int kVBase = kTile * kLdsRowK;                 // V rows follow the K rows
-constexpr int kStage = kVBase + kTile * kLdsRowV;
+constexpr int kLdsRow = kRowBytes;                 // unpadded rows (pieces permuted)
+constexpr int kVBase = kTile * kLdsRow;            // V rows follow the K rows
+constexpr int kStage = kVBase + kTile * kLdsRow;   // 8 KiB
+constexpr int kStages = 6;
 
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -115,6 +111,22 @@ struct Acc32 {
     float lsum;      // this lane's share (the other 16 keys sit in lane ^ 32)
 };
 
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// P.V operand of dim block mb out of the tile whose V rows start at LDS byte
+// vrow (row vrow0 of the stage, column vcol applied): two transposing reads,
+// rows vrow0 and vrow0 + 8 -- the lane's 8 k slots.  The piece at byte
+// column vcol of row r sits at slot ^ 4 (r & 3), i.e. 64 (q >> 2) bytes on,
+// which the caller folds into vcol; dim block mb flips bits 6-7.
+__device__ __forceinline__ u32x4 read_v_operand(unsigned vrow, int mb) {
+    const unsigned va = vrow ^ (64u * mb);
+    const uint2 x =
+        __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(size_t)va));
+    const uint2 y = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(size_t)(va + 8 * kLdsRow)));
+    return (u32x4){x.x, x.y, y.x, y.y};
+}
+
 // One step over a pair of 16-key tiles (32 keys) for the 32 columns.
 //  scores: S[32 keys x 32 columns] = K_pair . Q^T, 8 x v_mfma_f32_32x32x16_bf16;
 //          the lane holds column lane % 32 at keys 8 i + 4 (lane / 32) + j;
@@ -124,18 +136,35 @@ struct Acc32 {
 //          is key 16 kb + 8 i' + 4 h + j (h = lane / 32) -- the order in
 //          which the lane holds P -- and V arrives through the transposing
 //          LDS read in the same order.
-__device__ __forceinline__ void pair_update32(const char *stA, const char *stB,
+// stA / stB: LDS byte offsets of the pair's two stages.
+__device__ __forceinline__ void pair_update32(unsigned stA, unsigned stB,
                                               const bf16x8 (&qv)[8], int nv, bool okA, bool okB,
                                               float scale_log2, Acc32 &a, int lane) {
     const int col = lane & 31, half = lane >> 5;
-    const char *krow = (col < 16 ? stA : stB) + (col & 15) * kLdsRowK + half * 16;
+    // piece 2 kk + half of row krw sits at slot (2 kk + half) ^ krw
+    //   = 2 kk ^ (half ^ krw): the row's address with slot half ^ krw, xor 32 kk
+    const int krw = col & 15;
+    const unsigned kaddr = (col < 16 ? stA : stB) + (unsigned)(krw * kLdsRow) +
+                           (unsigned)(((half ^ krw) & 15) << 4);
     f32x16 S = {};
 #pragma unroll
     for (int kk = 0; kk < 8; kk++) {
-        const u32x4 kr = *(const u32x4 *)(krow + 32 * kk);
+        const u32x4 kr = *(const lds_u32x4 *)(size_t)(kaddr ^ (32u * kk));
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr), qv[kk], S, 0,
                                                     0, 0);
     }
+    // transposing V reads: lane q of each 16-lane group reads 4 dims of key
+    // row 8 i' + 4 half + q / 4 of the tile; lane i of the group receives
+    // one dim (dbase + i) of the 4 keys.  Tile A's operands are read here,
+    // so they arrive while the softmax runs; tile B's after it (registers).
+    const int q = lane & 15, g16 = lane >> 4;
+    const int vrow0 = 4 * half + (q >> 2);
+    const unsigned vcol = (unsigned)((16 * (g16 & 1) + 4 * (q & 3)) * 2 + 64 * (q >> 2));
+    const unsigned vrowA = stA + (unsigned)(kVBase + vrow0 * kLdsRow) + vcol;
+    const unsigned vrowB = stB + (unsigned)(kVBase + vrow0 * kLdsRow) + vcol;
+    u32x4 vA[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++) vA[mb] = read_v_operand(vrowA, mb);
     float s[16];
     // a valid column sees every key of the pair unless the pair reaches past
     // its row or holds a tile with an invalid block id: then mask
@@ -186,40 +215,26 @@ __device__ __forceinline__ void pair_update32(const char *stA, const char *stB,
                             pack_bf16x2(pr[8 * kb + 2], pr[8 * kb + 3]),
                             pack_bf16x2(pr[8 * kb + 4], pr[8 * kb + 5]),
                             pack_bf16x2(pr[8 * kb + 6], pr[8 * kb + 7])});
-    // transposing V reads: lane q of each 16-lane group reads 4 dims of key
-    // row 8 i' + 4 half + q / 4 of the tile; lane i of the group receives
-    // one dim (dbase + i) of the 4 keys
-    const int q = lane & 15, g16 = lane >> 4;
-    const int vrow0 = 4 * half + (q >> 2);
-    const int vcol = (16 * (g16 & 1) + 4 * (q & 3)) * 2;
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-        const char *vt = (kb == 0 ? stA : stB) + kVBase + vcol;
+    for (int mb = 0; mb < 4; mb++)
+        a.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vA[mb]), pk[0],
+                                                          a.o[mb], 0, 0, 0);
 #pragma unroll
-        for (int mb = 0; mb < 4; mb++) {
-            const uint2 x = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                           (__attribute__((address_space(3))) s16x4 *)(vt + vrow0 * kLdsRowV +
-                                                                        64 * mb)));
-            const uint2 y = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                           (__attribute__((address_space(3))) s16x4 *)(vt + (vrow0 + 8) *
-                                                                                 kLdsRowV +
-                                                                        64 * mb)));
-            a.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, (u32x4){x.x, x.y, y.x, y.y}), pk[kb], a.o[mb], 0, 0,
-                0);
-        }
-    }
+    for (int mb = 0; mb < 4; mb++)
+        a.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, read_v_operand(vrowB, mb)), pk[1], a.o[mb], 0, 0, 0);
 }
-constexpr int kStages = 4;
+// s_waitcnt operand that waits until at most n vector memory operations of
+// this wavefront are outstanding (the other counters untouched)
+constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 __global__ __launch_bounds__(kWgThreads)
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
 void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ tables,
                          const int32_t *__restrict__ cu_q, const int32_t *__restrict__ ctx_lens,
                          void *__restrict__ out) {
-    __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
+    __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
+    const unsigned lds0 = (unsigned)(size_t)(__attribute__((address_space(3))) char *)lds;
     const PrefillParams &p = args;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -278,61 +293,66 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
     const int bs_mask = (1 << log2bs) - 1;
     const int ntiles = (kmax + kTile - 1) / kTile;
     auto phys_of = [&](int t) -> int { return table[(min(t, ntiles - 1) * kTile) >> log2bs]; };
-    auto issue = [&](int t, int phys, u32x4 (&gr)[kPiecesPerThread]) {
+    // this wavefront's two 1 KiB quarters of every tile: quarter c = 2 wave + jj
+    // (0-3: K rows 4c .. 4c+3; 4-7: V rows 4(c-4) ..); lane l writes LDS bytes
+    // 16 l of the quarter: row 4 (c & 3) + l / 16, slot l % 16, which holds
+    // piece (l % 16) ^ r (K) or (l % 16) ^ 4 (r & 3) (V) of that row
+    const bool moves_k = wave < 2;
+    unsigned voff[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++) {
+        const int row = 4 * ((2 * wave + jj) & 3) + (lane >> 4);
+        const int sl = lane & 15;
+        const int piece = moves_k ? (sl ^ row) : (sl ^ (4 * (row & 3)));
+        voff[jj] = (unsigned)(row * kRowBytes + piece * 16);
+    }
+    // Buffer load of tile t (block id phys) into stage st.  Issued from an
+    // asm statement: a buffer-to-LDS load from the builtin makes the compiler
+    // wait for every such load in flight before any later LDS read (it
+    // cannot tell the stages apart), which would void the two-pair lead.
+    // The statement has no register outputs (the data goes to LDS); its
+    // completion is awaited explicitly before the barrier that publishes the
+    // stage.
+    auto load_tile = [&](int t, int st) {
+        const int phys = phys_of(t);
         const bool in = t < ntiles && (unsigned)phys < (unsigned)p.num_blocks;
         const int rows = in ? min(kTile, kmax - t * kTile) : 0;
         const size_t off = ((((size_t)(in ? phys : 0) * p.num_kv_heads + g) << log2bs) +
                             ((t * kTile) & bs_mask)) * (size_t)kRowBytes;
+        const uint64_t base = (uint64_t)(size_t)((moves_k ? kbase : vbase) + off);
+        typedef int i32x4v __attribute__((ext_vector_type(4)));
+        const i32x4v rs = {(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu),
+                           rows * kRowBytes, kRsrcWord3};
+        const unsigned m0base = lds0 + (unsigned)(st * kStage + 2 * wave * 1024);
 #pragma unroll
-        for (int j = 0; j < kPiecesPerThread; j++) {
-            const int c = tid + j * kWgThreads;
-            const int goff = ((c >> 4) & (kTile - 1)) * kRowBytes + (c & 15) * 16;
-            const bool of_k = wave * kWave + j * kWgThreads < kPieces / 2;
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)((of_k ? kbase : vbase) + off), (short)0, rows * kRowBytes, kRsrcWord3);
-            gr[j] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, goff, 0, kReuseAux));
+        for (int jj = 0; jj < 2; jj++) {
+            const unsigned m0v = __builtin_amdgcn_readfirstlane(m0base + jj * 1024);
+            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :
+                         : "s"(m0v), "v"(voff[jj]), "s"(rs)
+                         : "memory", "m0");
         }
     };
-    auto stage_write = [&](int st, const u32x4 (&gr)[kPiecesPerThread]) {
-        char *base = lds + st * kStage;
-#pragma unroll
-        for (int j = 0; j < kPiecesPerThread; j++) {
-            const int c = tid + j * kWgThreads;
-            const int row = c >> 4;
-            const int lo = row < kTile ? row * kLdsRowK : kVBase + (row - kTile) * kLdsRowV;
-            *(u32x4 *)(base + lo + (c & 15) * 16) = gr[j];
-        }
-    };
-
-    const int ntiles2 = (ntiles + 1) & ~1;
-    u32x4 gr[2][kPiecesPerThread];
-    int phA = phys_of(0), phB = phys_of(1);
-    issue(0, phA, gr[0]);
-    issue(1, phB, gr[1]);
-    stage_write(0, gr[0]);
-    stage_write(1, gr[1]);
-    int phC = phys_of(2), phD = phys_of(3);
-    issue(2, phC, gr[0]);
-    issue(3, phD, gr[1]);
+    const int npairs = (ntiles + 1) >> 1;
+    load_tile(0, 0);
+    load_tile(1, 1);
+    load_tile(2, 2);
+    load_tile(3, 3);
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(4));
     lds_barrier();
-    for (int t = 0; t < ntiles; t += 2) {
-        const int sa = t & 3;
-        const bool okA = (unsigned)phA < (unsigned)p.num_blocks;
-        const bool okB = (unsigned)phB < (unsigned)p.num_blocks;
-        pair_update32(lds + sa * kStage, lds + (sa + 1) * kStage, qv, ncol - t * kTile, okA, okB,
-                      p.scale_log2, a, lane);
-        if (t + 2 < ntiles2) {
-            stage_write((t + 2) & 3, gr[0]);
-            stage_write((t + 3) & 3, gr[1]);
-        }
-        phA = phC;
-        phB = phD;
-        phC = phys_of(t + 4);
-        phD = phys_of(t + 5);
-        issue(t + 4, phC, gr[0]);
-        issue(t + 5, phD, gr[1]);
+    int sp = 0;   // stage pair (0, 1, 2) of pair p
+    for (int pp = 0; pp < npairs; pp++) {
+        const int t = 2 * pp;
+        const int sw = sp == 0 ? 2 : sp - 1;   // pair p+2 goes where pair p-1 was
+        load_tile(t + 4, 2 * sw);
+        load_tile(t + 5, 2 * sw + 1);
+        const bool okA = (unsigned)phys_of(t) < (unsigned)p.num_blocks;
+        const bool okB = (unsigned)phys_of(t + 1) < (unsigned)p.num_blocks;
+        pair_update32(lds0 + (unsigned)(2 * sp * kStage), lds0 + (unsigned)((2 * sp + 1) * kStage),
+                      qv, ncol - t * kTile, okA, okB, p.scale_log2, a, lane);
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(4));
         lds_barrier();
+        sp = sp == 2 ? 0 : sp + 1;
     }
     const float lsum = xor32_sum(a.lsum);
     if (ok) {
