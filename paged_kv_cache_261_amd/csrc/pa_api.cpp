@@ -116,7 +116,7 @@ int resolve_partition(int partition_size, int num_seqs, int num_q_heads, int num
 
 struct WorkspaceLayout {
     size_t m_off, l_off, acc_off, total;
-    size_t cost_off, pos_off, dir_off;   // shared-prefix mode
+    size_t cost_off, pos_off;            // shared-prefix mode
     int num_partitions;
     int pack, num_packs, max_tiles;      // shared-prefix mode
 };
@@ -125,7 +125,7 @@ WorkspaceLayout layout(int num_seqs, int num_q_heads, int head_dim, int max_cont
                        int partition, int group = 1) {
     WorkspaceLayout w{};
     if (partition == PA_PARTITION_SHARED) {
-        // cost [P] | items [P][pack * max_tiles][4] | dir [W][2] | m, l [W][2][32] |
+        // cost [P] | items [P][pack * max_tiles][4] | m, l [W][2][32] |
         // acc [W][2][32][head_dim]
         const size_t slots = (size_t)kSharedWaves * 2 * pa::kMaxCols;
         w.pack = pack_of(group);
@@ -133,9 +133,8 @@ WorkspaceLayout layout(int num_seqs, int num_q_heads, int head_dim, int max_cont
         w.max_tiles = (max_context_len + 15) / 16;
         w.cost_off = 0;
         w.pos_off = round256((size_t)w.num_packs * sizeof(int32_t));
-        w.dir_off = w.pos_off + round256((size_t)w.num_packs * w.pack * w.max_tiles * 4 *
-                                         sizeof(int32_t));
-        w.m_off = w.dir_off + round256((size_t)kSharedWaves * 2 * sizeof(int32_t));
+        w.m_off = w.pos_off + round256((size_t)w.num_packs * w.pack * w.max_tiles * 4 *
+                                       sizeof(int32_t));
         w.l_off = w.m_off + round256(slots * sizeof(float));
         w.acc_off = w.l_off + round256(slots * sizeof(float));
         w.total = w.acc_off + round256(slots * head_dim * sizeof(float));
@@ -299,7 +298,6 @@ pa::SharedParams shared_params(const DecodeArgs &a, const WorkspaceLayout &w, ch
     p.num_waves = kSharedWaves;
     p.ws_cost = (int *)(ws + w.cost_off);
     p.ws_items = (int *)(ws + w.pos_off);
-    p.ws_dir = (int *)(ws + w.dir_off);
     p.ws_m = (float *)(ws + w.m_off);
     p.ws_l = (float *)(ws + w.l_off);
     p.ws_acc = (float *)(ws + w.acc_off);

@@ -25,10 +25,11 @@
 //     item is one tile load and one update of the columns of its members, so
 //     a share may start or end anywhere.  A pack a wavefront covers whole is
 //     finished in place; otherwise its state goes to one of the wavefront's
-//     two partial slots (only its first and last pack can be partial) and
-//     the slot is recorded in a small directory.
-//  3. reduce_shared_kernel: per (KV head, pack, column), merge the recorded
-//     pieces by log-sum-exp.
+//     two partial slots: slot 0 for the first unit of its share, slot 1 for
+//     the last (only those two can be partial).
+//  3. reduce_shared_kernel: per (KV head, pack, column), merge the pieces
+//     by log-sum-exp; which wavefronts and slots hold them follows from the
+//     split alone.
 #include "pa_mfma_tile.h"
 
 namespace pa {
@@ -56,6 +57,18 @@ __global__ __launch_bounds__(kPlanMaxThreads) void plan_shared_kernel(const Shar
         n[i] = b < p.num_seqs ? clamp_ctx(p.context_lens[b], p.max_context_len) : 0;
         maxT = max(maxT, (n[i] + kTile - 1) / kTile);
     }
+    // the block ids of the first chunk of tile indices, read alongside the
+    // context lengths rather than after them (one memory round trip, not
+    // two): every index below max_tiles is inside the table row
+    int id0[NPK];
+#pragma unroll
+    for (int i = 0; i < NPK; i++) {
+        const int b = k * NPK + i;
+        id0[i] = b < p.num_seqs && tid < p.max_tiles
+                     ? p.block_tables[(size_t)b * p.max_blocks_per_seq +
+                                      ((tid * kTile) >> p.log2_block)]
+                     : -1;
+    }
     int4 *items = (int4 *)p.ws_items + (size_t)k * NPK * p.max_tiles;
     int running = 0;
     for (int t0 = 0; t0 < maxT; t0 += blockDim.x) {
@@ -64,10 +77,11 @@ __global__ __launch_bounds__(kPlanMaxThreads) void plan_shared_kernel(const Shar
         bool v[NPK];
 #pragma unroll
         for (int i = 0; i < NPK; i++) {
-            v[i] = t * kTile < n[i];
-            id[i] = v[i] ? p.block_tables[(size_t)(k * NPK + i) * p.max_blocks_per_seq +
-                                          ((t * kTile) >> p.log2_block)]
-                         : -1;
+            v[i] = t * kTile < n[i];          // then t < max_tiles
+            id[i] = !v[i] ? -1
+                    : t0 == 0 ? id0[i]
+                              : p.block_tables[(size_t)(k * NPK + i) * p.max_blocks_per_seq +
+                                               ((t * kTile) >> p.log2_block)];
         }
         int cost = 0;
 #pragma unroll
@@ -135,7 +149,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PA_SHARED
 void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ ctx_lens,
                           void *__restrict__ out, float *__restrict__ ws_m,
                           float *__restrict__ ws_l, float *__restrict__ ws_acc,
-                          int *__restrict__ ws_dir, const int *__restrict__ ws_cost,
+                          const int *__restrict__ ws_cost,
                           const int4 *__restrict__ ws_items) {
     // restrict arguments: the stores cannot alias the item lists, so the
     // per-item reads stay on the scalar unit
@@ -194,13 +208,12 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
     // tile loads holds up the wait for the later one.  The state of the
     // wave's first pack waits in `pend` until the next pack's first loads
     // are in flight, or, if that pack is the wave's last, until the end.
-    // Partial states go to the wave's two slots (only its first and last
-    // packs can be partial); dir[] records which unit each slot holds.
+    // Partial states go to the wave's two slots: slot 0 holds the share's
+    // first unit, slot 1 its last (only those two can be partial).
     Acc pend[NCG];
     bool have_pend = false, pend_whole = false;
     int pend_g = 0, pend_k = 0, pend_slot = 0;
     int slot = 0;
-    int dir0 = -1, dir1 = -1;
     auto emit = [&](const Acc (&st)[NCG], bool whole, int g, int k, int sl) {
 #pragma unroll
         for (int cg = 0; cg < NCG; cg++) {
@@ -347,12 +360,8 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
         const bool whole = q_begin == 0 && q_end == Uk;
 #pragma unroll
         for (int cg = 0; cg < NCG; cg++) acc_finish(a[cg]);
-        int sl = 0;
-        if (!whole) {
-            sl = slot;
-            if (slot == 0) dir0 = g * NPACK + k; else dir1 = g * NPACK + k;
-            slot = 1;
-        }
+        const int sl = slot;             // 0 for the share's first unit, then 1
+        slot = 1;
         if (have_pend) {                 // this is the wave's last pack
             emit(pend, pend_whole, pend_g, pend_k, pend_slot);
             have_pend = false;
@@ -368,37 +377,33 @@ void decode_shared_kernel(const SharedParams args, const int32_t *__restrict__ c
         }
     }
     if (have_pend) emit(pend, pend_whole, pend_g, pend_k, pend_slot);
-    if (lane == 0) {
-        ws_dir[2 * w] = dir0;
-        ws_dir[2 * w + 1] = dir1;
-    }
 }
 
 // ---------------------------------------------------------------------------
 // 3. Merge.
 // ---------------------------------------------------------------------------
 // One workgroup of 4 wavefronts per (KV head, pack) unit.  The unit's
-// pieces -- the partial slots whose directory entry names it, among the
-// wavefronts whose shares overlap the unit -- are listed in ascending order;
-// then all 32 columns are merged at once, 8 threads per column and 16 dims
-// per thread, pieces summed in list order.  Every wavefront finds the
-// unit's position and lists the pieces itself (into its own LDS region), so
-// the workgroup needs no barrier; up to kDirect pieces are loaded in one
-// round and merged in registers.
+// position in the item stream gives its pieces without a lookup: with C
+// items per share, the unit's items [start, start + U) lie in the shares of
+// wavefronts first = start / C .. last = (start + U - 1) / C.  One share
+// (first == last) finished it in place.  Otherwise wavefront `first` holds
+// a piece in slot 0 if its share starts exactly at the unit (the unit is
+// its first) and in slot 1 if not (the unit is its last), and every later
+// wavefront up to `last` in slot 0 (its share starts inside the unit).
+// All 32 columns are merged at once, 8 threads per column and 16 dims per
+// thread, pieces summed in ascending wavefront order; up to kDirect pieces
+// are loaded in one round and merged in registers.
 constexpr int kReduceThreads = 256;
-constexpr int kReduceWaves = kReduceThreads / kWave;
 constexpr int kDirect = 6;
 
 template <int NPK, int NCG>
 __global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
-    const SharedParams p, const int *__restrict__ ws_dir, const int *__restrict__ ws_cost) {
-    extern __shared__ int lds[];                   // pieces[kReduceWaves][2 W]
+    const SharedParams p, const int *__restrict__ ws_cost) {
     const int unit = blockIdx.x;                   // g * NPACK + k
     const int NPACK = p.num_packs;
     const int k = unit % NPACK, g = unit / NPACK;
     const int G = p.group;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    int *pieces = lds + wave * 2 * p.num_waves;
+    const int tid = threadIdx.x, lane = tid % kWave;
 
     // position of the unit in the item stream (as the decode kernel split it)
     const int U = __builtin_amdgcn_readfirstlane(ws_cost[k]);
@@ -414,21 +419,19 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
         all += __shfl_xor(all, o);
     }
     const int S = before, TT = all;
-    int first = 0, last = -1;
+    int first = 0, last = 0, first_slot = 0;
     if (U > 0) {
         const int C = (TT * p.num_kv_heads + p.num_waves - 1) / p.num_waves;
         const int start = g * TT + S;
         first = start / C;
         last = (start + U - 1) / C;
+        first_slot = start == first * C ? 0 : 1;
     }
-    int npieces = 0;
-    for (int e0 = 2 * first; e0 < 2 * last + 2; e0 += kWave) {
-        const int e = e0 + lane;
-        const bool hit = e < 2 * last + 2 && ws_dir[e] == unit;
-        const unsigned long long m = __ballot(hit);
-        if (hit) pieces[npieces + __builtin_popcountll(m & ((1ull << lane) - 1))] = e;
-        npieces += __builtin_popcountll(m);
-    }
+    const int npieces = last - first + 1;
+    // piece q: wavefront first + q, slot (q == 0 ? first_slot : 0)
+    auto piece_row = [&](int q, int c) -> size_t {
+        return ((size_t)(first + q) * 2 + (q == 0 ? first_slot : 0)) * kMaxCols + c;
+    };
 
     // 8 lanes per column, 16 dims per lane: the 32 columns at once
     const int c = tid / 8, sub = tid % 8;
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
         *(uint4 *)(o + 8) = make_uint4(0u, 0u, 0u, 0u);
         return;
     }
-    if (npieces == 0) return;                       // finished by one wavefront
+    if (npieces == 1) return;                       // finished by one wavefront
     float num[16], den = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; e++) num[e] = 0.f;
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
 #pragma unroll
         for (int q = 0; q < kDirect; q++) {
             if (q < npieces) {
-                const size_t prow = (size_t)pieces[q] * kMaxCols + c;
+                const size_t prow = piece_row(q, c);
                 mq[q] = p.ws_m[prow];
                 lq[q] = p.ws_l[prow];
                 const float4 *src = (const float4 *)(p.ws_acc + prow * kD + 16 * sub);
@@ -483,10 +486,10 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_shared_kernel(
         }
     } else {
         float M = -INFINITY;
-        for (int q = 0; q < npieces; q++) M = fmaxf(M, p.ws_m[(size_t)pieces[q] * kMaxCols + c]);
+        for (int q = 0; q < npieces; q++) M = fmaxf(M, p.ws_m[piece_row(q, c)]);
         if (M != -INFINITY) {
             for (int q = 0; q < npieces; q++) {
-                const size_t prow = (size_t)pieces[q] * kMaxCols + c;
+                const size_t prow = piece_row(q, c);
                 const float mq = p.ws_m[prow];
                 const float wq = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - M);
                 den = fmaf(wq, p.ws_l[prow], den);
@@ -522,14 +525,13 @@ static hipError_t launch_shared_t(const SharedParams &p, int phase, hipStream_t 
         hipLaunchKernelGGL(plan_shared_kernel<NPK>, dim3(p.num_packs), dim3(plan_threads), 0,
                            stream, p);
         hipLaunchKernelGGL((decode_shared_kernel<NPK, NCG>), dim3(p.num_waves), dim3(kWave), 0,
-                           stream, p, p.context_lens, p.out, p.ws_m, p.ws_l, p.ws_acc, p.ws_dir,
-                           p.ws_cost, (const int4 *)p.ws_items);
+                           stream, p, p.context_lens, p.out, p.ws_m, p.ws_l, p.ws_acc, p.ws_cost,
+                           (const int4 *)p.ws_items);
     }
     if (phase & 2)
         hipLaunchKernelGGL((reduce_shared_kernel<NPK, NCG>),
-                           dim3((unsigned)p.num_kv_heads * p.num_packs), dim3(kReduceThreads),
-                           (size_t)kReduceWaves * 2 * p.num_waves * sizeof(int), stream, p,
-                           p.ws_dir, p.ws_cost);
+                           dim3((unsigned)p.num_kv_heads * p.num_packs), dim3(kReduceThreads), 0,
+                           stream, p, p.ws_cost);
     return hipGetLastError();
 }
 

@@ -83,7 +83,6 @@ struct SharedParams {
     int num_waves;            // persistent wavefronts
     int *ws_cost;             // [num_packs] items (distinct tiles) per pack
     int *ws_items;            // [num_packs][pack * max_tiles] item records, 4 ints each
-    int *ws_dir;              // [W][2] pack unit held by each partial slot, or -1
     float *ws_m;              // [W][2][32]
     float *ws_l;              // [W][2][32]
     float *ws_acc;            // [W][2][32][128]

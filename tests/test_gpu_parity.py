@@ -997,10 +997,12 @@ def prefill_gpu_case(rng, chunks, prefixes, hq, hkv, bs, nb_extra=5):
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 16])
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
 def test_prefill_matches_oracle(G, bs):
     """Chunks of 0, 1, a few and many rows, over empty, short and long
-    prefixes, lengths off every tile and wavefront boundary; unused slots NaN."""
+    prefixes, lengths off every tile and wavefront boundary; unused slots NaN.
+    Block sizes from one tile per block to sixteen (a tile's rows start
+    inside its block)."""
     rng = np.random.default_rng(100 * G + bs)
     chunks = [1, 0, 7, 40, 33, 100, 5]
     prefixes = [0, 12, 0, 1, 250, 77, 600]
