@@ -354,6 +354,10 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
         lds_barrier();
         sp = sp == 2 ? 0 : sp + 1;
     }
+    // The last four loads (tiles past the last pair, zero-sized) may still be
+    // in flight; the compiler does not count loads issued from asm, so drain
+    // them here, before the workgroup's LDS can be handed to another.
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     const float lsum = xor32_sum(a.lsum);
     if (ok) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
