@@ -60,7 +60,7 @@ struct ReduceParams {
 };
 
 // Shared-prefix decode (matrix-core path): packs of `pack` consecutive
-// sequences share one wavefront's 16 columns.
+// sequences share one wavefront's 32 columns (two groups of 16).
 struct SharedParams {
     void *out;
     const void *q;
