@@ -383,7 +383,7 @@ def random_decode_case(seed):
     return dtype, d, G, bs, q, kc, vc, tab, np.array(ctxs, dtype=np.int32)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_decode_problems(seed):
     """Seeded random shapes against the oracle in every mode and kernel the
     shape admits (single pass, fixed partitions, balanced, shared, auto)."""
@@ -1225,3 +1225,40 @@ def test_prefill_negative_scale_matches_oracle():
         ref = pao.prefill_concat(q, kc, vc, tab, cu, ctx, scale)
         got = gpu_prefill(q, H.to_dev(kc), H.to_dev(vc), tab, cu, ctx, scale)
         H.assert_close_to_oracle(got, ref, "bf16", f"prefill with scale {scale}")
+
+
+def random_prefill_case(seed):
+    """One seeded random prefill problem: even seeds on the matrix-core shape
+    (bf16, head_dim 128, block size 16-256), odd seeds on any shape; random
+    group size, chunk and prefix mix (empty, one row, tile and block edges,
+    long), the pool a random permutation with spare blocks."""
+    rng = np.random.default_rng(3000 + seed)
+    if seed % 2 == 0:
+        dtype, d, bs = "bf16", 128, int(rng.choice([16, 32, 64, 128, 256]))
+    else:
+        dtype = ["f32", "bf16"][int(rng.integers(2))]
+        d = int(rng.choice([16, 32, 64, 128, 256]))
+        bs = int(rng.choice([1, 2, 4, 8, 16, 64]))
+    G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 16]))
+    hkv = int(rng.integers(1, 4))
+    B = int(rng.integers(1, 10))
+    edge = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65]
+    chunks = [int(rng.choice(edge)) if rng.random() < 0.5 else int(rng.integers(1, 200))
+              for _ in range(B)]
+    prefixes = [int(rng.choice(edge + [bs, bs + 1])) if rng.random() < 0.5
+                else int(rng.integers(0, 800)) for _ in range(B)]
+    q, cu, ctx, kc, vc, tab = prefill_case_any(rng, chunks, prefixes, hkv * G, hkv, d, bs, dtype)
+    return dtype, d, G, bs, q, cu, ctx, kc, vc, tab
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_prefill_problems(seed):
+    """Seeded random prefill problems against the oracle (the library picks
+    the matrix-core or the vector kernel by shape)."""
+    dtype, d, G, bs, q, cu, ctx, kc, vc, tab = random_prefill_case(seed)
+    note(f"[gpu parity] random prefill {seed}: {dtype} d {d} G {G} bs {bs} B {len(ctx)} "
+         f"rows {int(cu[-1])}")
+    scale = 1 / math.sqrt(d)
+    ref = pao.prefill_concat(q, kc, vc, tab, cu, ctx, scale)
+    got = gpu_prefill(q, H.to_dev(kc), H.to_dev(vc), tab, cu, ctx, scale)
+    H.assert_close_to_oracle(got, ref, dtype, f"random prefill {seed}")
