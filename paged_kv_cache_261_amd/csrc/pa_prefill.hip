@@ -309,7 +309,8 @@ void prefill_mfma_kernel(const PrefillParams args, const int32_t *__restrict__ t
     // Buffer load of tile t (block id phys) into stage st.  Issued from an
     // asm statement: a buffer-to-LDS load from the builtin makes the compiler
     // wait for every such load in flight before any later LDS read (it
-    // cannot tell the stages apart), which would void the two-pair lead.
+    // cannot tell the stages apart, even as separate LDS arrays addressed
+    // through their own pointers), which would void the two-pair lead.
     // The statement has no register outputs (the data goes to LDS); its
     // completion is awaited explicitly before the barrier that publishes the
     // stage.
